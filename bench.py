@@ -1,0 +1,379 @@
+#!/usr/bin/env python3
+"""Benchmark of the scaled 8-bit GEMM hot path on one MI355X.
+
+Headline (``value``): the prefill step — per-token-group FP8 quantization of a
+bf16 activation [4096, 7168] (groups of 128) followed by the [128,128]-block-
+scaled FP8 GEMM against W [7168, 7168] with bf16 output — as whole-step
+TFLOP/s (2*M*N*K per step over the measured step time). The dominant kernel
+(the GEMM) is timed on its own with HIP events around each of its launches in
+the timed steps, and reported against the dense FP8 MFMA peak (roofline).
+
+Secondary paths, each timed the same way and reported under ``paths``:
+decode block32 GEMM (M in {1, 4, 16, 64}, N=4096, K=7168, UE8M0 group-32
+activation quant) as GB/s against HBM, with weights rotated over enough copies
+that the 256 MB Infinity Cache cannot hold them; the quant kernel alone;
+INT8 W8A8 (2048 x 8192 x 8192, per-token x per-channel); the MoE step
+(routing + quant + expert-grouped GEMM with fused gather/un-permute).
+
+The CPU oracle is timed on a bounded sample of the prefill workload (a
+subset of rows) as ``cpu_baseline``.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_INT8_TOPS = 5000.0    # MI355X dense INT8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+EPS = 1e-10
+MALL_BYTES = 256 << 20
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class KernelTimer:
+    """HIP events around launches on the current stream; mean/median in us."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __enter__(self):
+        self.s = self.torch.cuda.Event(enable_timing=True)
+        self.e = self.torch.cuda.Event(enable_timing=True)
+        self.s.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.e.record()
+        self.pairs.append((self.s, self.e))
+        return False
+
+    def us(self):
+        v = [s.elapsed_time(e) * 1e3 for s, e in self.pairs]
+        return {"mean": statistics.fmean(v), "median": statistics.median(v),
+                "p10": sorted(v)[len(v) // 10], "p90": sorted(v)[(len(v) * 9) // 10], "n": len(v)}
+
+
+def source_sha(*names: str) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "int8_quantized_gemm_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str, sha: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, only
+    while the kernel source still matches the one that was profiled."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = table.get(f"{kernel}:{workload}")
+    if not rec or rec.get("source_sha") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+def bench_prefill(torch, q8, synth, steps, warmup):
+    M, N, K, blk = 4096, 7168, 7168, 128
+    dev = "cuda:0"
+    x = synth.activations(M, K, "bf16", seed=0).to(dev)
+    Wq, Ws = synth.fp8_block_weights(N, K, blk, blk, seed=0)
+    Wq, Ws = Wq.to(dev), Ws.to(dev)
+    aq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+    As = torch.empty((M, K // blk), dtype=torch.float32, device=dev)
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def step(gt=None, qt=None):
+        if qt:
+            with qt:
+                q8.quant_8bit(x, aq, As, blk, EPS, -448.0, 448.0, False)
+        else:
+            q8.quant_8bit(x, aq, As, blk, EPS, -448.0, 448.0, False)
+        if gt:
+            with gt:
+                q8.blockwise_scaled_mm(aq, Wq, As, Ws, torch.bfloat16, block=(blk, blk), out=D)
+        else:
+            q8.blockwise_scaled_mm(aq, Wq, As, Ws, torch.bfloat16, block=(blk, blk), out=D)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # step time: plain launches, bracketed by synchronize
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    # kernel durations: events around each launch, on the launch stream
+    gt, qt = KernelTimer(torch), KernelTimer(torch)
+    for _ in range(steps):
+        step(gt, qt)
+    torch.cuda.synchronize()
+    flops = 2.0 * M * N * K
+    g_us = gt.us()
+    return {
+        "ms_per_step": ms_per_step,
+        "tflops_step": flops / (ms_per_step * 1e-3) / 1e12,
+        "gemm_us": g_us, "quant_us": qt.us(),
+        "gemm_tflops": flops / (g_us["mean"] * 1e-6) / 1e12,
+        "shape": (M, N, K, blk),
+        "x": x, "Wq": Wq, "Ws": Ws,
+    }
+
+
+def bench_decode(torch, q8, synth, reps):
+    N, K, blk = 4096, 7168, 32
+    dev = "cuda:0"
+    wbytes = N * K
+    copies = max(2, -(-(MALL_BYTES + (64 << 20)) // wbytes))
+    Wq0, Ws0 = synth.fp8_block_weights(N, K, blk, blk, seed=0)
+    Ws = Ws0.to(dev)
+    Ws_list = [Ws.clone() for _ in range(copies)]
+    W_list = [Wq0.to(dev) for _ in range(copies)]
+    out = {}
+    for M in (1, 4, 16, 64):
+        x = synth.activations(M, K, "bf16", outlier_frac=0.01, seed=0).to(dev)
+        aq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+        As = torch.empty((M, K // blk), dtype=torch.float32, device=dev)
+        D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        gt, qt = KernelTimer(torch), KernelTimer(torch)
+        for i in range(reps + 10):
+            c = i % copies
+            timed = i >= 10
+            if timed:
+                with qt:
+                    q8.quant_8bit(x, aq, As, blk, EPS, -448.0, 448.0, True)
+                with gt:
+                    q8.blockwise_scaled_mm(aq, W_list[c], As, Ws_list[c], torch.bfloat16,
+                                           block=(blk, blk), out=D)
+            else:
+                q8.quant_8bit(x, aq, As, blk, EPS, -448.0, 448.0, True)
+                q8.blockwise_scaled_mm(aq, W_list[c], As, Ws_list[c], torch.bfloat16,
+                                       block=(blk, blk), out=D)
+        torch.cuda.synchronize()
+        g = gt.us()
+        nbytes = wbytes + Ws.numel() * 4 + M * K + M * (K // blk) * 4 + M * N * 2
+        gbs = nbytes / (g["median"] * 1e-6) / 1e9
+        out[f"M{M}"] = {"gemm_us": round(g["median"], 3), "gemm_us_p10": round(g["p10"], 3),
+                        "gemm_us_p90": round(g["p90"], 3), "quant_us": round(qt.us()["median"], 3),
+                        "algorithmic_bytes": nbytes, "GB/s": round(gbs, 1),
+                        "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                        "tflops": round(2.0 * M * N * K / (g["median"] * 1e-6) / 1e12, 2)}
+    out["weight_copies_rotated"] = copies
+    return out
+
+
+def bench_quant(torch, q8, synth, reps):
+    M, K = 4096, 7168
+    dev = "cuda:0"
+    copies = max(2, -(-(MALL_BYTES + (64 << 20)) // (M * K * 2)))
+    base = synth.activations(M, K, "bf16", seed=0).to(dev)
+    xs = [base.clone() for _ in range(copies)]
+    aq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+    res = {}
+    for g, ue in ((128, False), (32, True)):
+        As = torch.empty((M, K // g), dtype=torch.float32, device=dev)
+        t = KernelTimer(torch)
+        for i in range(reps + 10):
+            if i >= 10:
+                with t:
+                    q8.quant_8bit(xs[i % copies], aq, As, g, EPS, -448.0, 448.0, ue)
+            else:
+                q8.quant_8bit(xs[i % copies], aq, As, g, EPS, -448.0, 448.0, ue)
+        torch.cuda.synchronize()
+        u = t.us()
+        nbytes = M * K * 2 + M * K + M * (K // g) * 4
+        gbs = nbytes / (u["median"] * 1e-6) / 1e9
+        res[f"g{g}{'_ue8m0' if ue else ''}"] = {"us": round(u["median"], 3), "algorithmic_bytes": nbytes,
+                                                "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    res["input_copies_rotated"] = copies
+    return res
+
+
+def bench_int8(torch, q8, synth, reps):
+    M, N, K = 2048, 8192, 8192
+    dev = "cuda:0"
+    x = synth.activations(M, K, "bf16", seed=0).to(dev)
+    Wq, ws = synth.int8_weights(N, K, per_channel=True, seed=0)
+    Wq, ws = Wq.to(dev), ws.to(dev)
+    b = synth.bias(N, seed=0).to(dev)
+    qa = torch.empty((M, K), dtype=torch.int8, device=dev)
+    sa = torch.empty((M, 1), dtype=torch.float32, device=dev)
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    gt, qt = KernelTimer(torch), KernelTimer(torch)
+    for i in range(reps + 5):
+        if i >= 5:
+            with qt:
+                q8.quant_8bit(x, qa, sa, K, EPS, -128.0, 127.0, False)
+            with gt:
+                q8.scaled_mm_int8(qa, Wq, sa, ws, torch.bfloat16, b, out=D)
+        else:
+            q8.quant_8bit(x, qa, sa, K, EPS, -128.0, 127.0, False)
+            q8.scaled_mm_int8(qa, Wq, sa, ws, torch.bfloat16, b, out=D)
+    torch.cuda.synchronize()
+    g = gt.us()
+    tops = 2.0 * M * N * K / (g["median"] * 1e-6) / 1e12
+    return {"gemm_us": round(g["median"], 2), "quant_us": round(qt.us()["median"], 2),
+            "TOP/s": round(tops, 1), "frac_int8_peak": round(tops / PEAK_INT8_TOPS, 4)}
+
+
+def bench_moe(torch, q8, synth, reps):
+    T, E, topk, N, K, blk = 4096, 64, 8, 2048, 7168, 128
+    dev = "cuda:0"
+    ids = synth.zipf_topk_ids(T, E, topk, seed=0).to(dev)
+    x = synth.activations(T, K, "bf16", seed=0).to(dev)
+    W, Ws = synth.fp8_block_weights(N, K, blk, blk, experts=E, seed=0)
+    W, Ws = W.to(dev), Ws.to(dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    ps1 = torch.empty((E, 3), dtype=torch.int32, device=dev)
+    ps2 = torch.empty((E, 3), dtype=torch.int32, device=dev)
+    ip = torch.empty(T * topk, dtype=torch.int32, device=dev)
+    op = torch.empty(T * topk, dtype=torch.int32, device=dev)
+    aq = torch.empty((T, K), dtype=torch.float8_e4m3fn, device=dev)
+    As = torch.empty((T, K // blk), dtype=torch.float32, device=dev)
+    D = torch.empty((T * topk, N), dtype=torch.bfloat16, device=dev)
+    rt, qt, gt = KernelTimer(torch), KernelTimer(torch), KernelTimer(torch)
+    for i in range(reps + 3):
+        timed = i >= 3
+        with (rt if timed else _Null()):
+            q8.moe_mm_data(ids, off, ps1, ps2, ip, op, E, N, K)
+        with (qt if timed else _Null()):
+            q8.quant_8bit(x, aq, As, blk, EPS, -448.0, 448.0, False)
+        with (gt if timed else _Null()):
+            q8.grouped_blockwise_scaled_mm(D, aq, W, As, Ws, off, ps1, a_map=ip, c_map=op)
+    torch.cuda.synchronize()
+    g = gt.us()
+    step_us = rt.us()["median"] + qt.us()["median"] + g["median"]
+    flops = 2.0 * T * topk * N * K
+    nbytes = E * N * K + T * K + T * topk * N * 2 + Ws.numel() * 4 + T * (K // blk) * 4
+    return {"routing_us": round(rt.us()["median"], 2), "quant_us": round(qt.us()["median"], 2),
+            "grouped_gemm_us": round(g["median"], 2),
+            "gemm_tflops": round(flops / (g["median"] * 1e-6) / 1e12, 1),
+            "frac_fp8_peak": round(flops / (g["median"] * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "gemm_GB/s_fused": round(nbytes / (g["median"] * 1e-6) / 1e9, 1),
+            "step_tflops": round(flops / (step_us * 1e-6) / 1e12, 1)}
+
+
+class _Null:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        return False
+
+
+def cpu_baseline(pre, rows: int):
+    """The oracle as it stands, on the first ``rows`` rows of the prefill
+    workload: quantize those rows, then the block-scaled GEMM against all of W."""
+    import numpy as np
+
+    from oracle import gemm as og
+    from oracle import quant as oq
+    M, N, K, blk = pre["shape"]
+    x = pre["x"][:rows].float().cpu().numpy()
+    Wq = pre["Wq"].cpu().numpy()
+    Ws = pre["Ws"].cpu().numpy()
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=None)
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    aq, As = oq.per_token_group(x, blk, EPS, -448.0, 448.0, False, "e4m3")
+    og.blockwise_scaled_mm(aq, As, Wq, Ws, blk, blk)
+    dt = time.perf_counter() - t0
+    _ = np
+    return {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": threads or len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"prefill rows 0..{rows - 1} of {M} (quant + block GEMM, N={N}, K={K}), {dt:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-rows", type=int, default=512, help="prefill rows for the oracle baseline")
+    ap.add_argument("--skip-secondary", action="store_true", help="headline prefill only")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import int8_quantized_gemm_amd as q8
+    import synth
+
+    torch.cuda.init()
+    log(f"device {torch.cuda.get_device_name(0)}")
+    pre = bench_prefill(torch, q8, synth, args.steps, args.warmup)
+    log(f"prefill: {pre['ms_per_step']:.3f} ms/step, GEMM {pre['gemm_us']['mean']:.1f} us "
+        f"= {pre['gemm_tflops']:.0f} TFLOP/s")
+    M, N, K, blk = pre["shape"]
+    sha = source_sha("gemm_block.hip", "tile_common.h", "q8_device.h")
+    roof = {"bound": "mfma", "achieved": round(pre["gemm_tflops"], 1), "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(pre["gemm_tflops"] / PEAK_FP8_TFLOPS, 4),
+            "traffic": measured_traffic("gemm_tile", "prefill_4096x7168x7168", sha),
+            "kernel": "gemm_tile (block-FP8, [128,128])",
+            "kernel_us": {k: round(v, 2) for k, v in pre["gemm_us"].items()}}
+    paths = {"prefill_quant_us": {k: round(v, 2) for k, v in pre["quant_us"].items()}}
+    if not args.skip_secondary:
+        reps = max(args.steps, 50)
+        paths["decode_block32"] = bench_decode(torch, q8, synth, max(reps, 200))
+        log(f"decode: {json.dumps(paths['decode_block32'])}")
+        paths["quant_4096x7168"] = bench_quant(torch, q8, synth, max(reps, 200))
+        log(f"quant: {json.dumps(paths['quant_4096x7168'])}")
+        paths["int8_2048x8192x8192"] = bench_int8(torch, q8, synth, reps)
+        log(f"int8: {json.dumps(paths['int8_2048x8192x8192'])}")
+        paths["moe_4096tok_e64_top8"] = bench_moe(torch, q8, synth, reps)
+        log(f"moe: {json.dumps(paths['moe_4096tok_e64_top8'])}")
+    cpu = cpu_baseline(pre, args.cpu_rows) if args.cpu_rows > 0 else None
+    line = {
+        "metric": "TFLOP/s & % fp8 MFMA peak (prefill), GB/s & % HBM (decode M≤16)",
+        "value": round(pre["tflops_step"], 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": "prefill: group-128 FP8 activation quant + [128,128]-block-scaled FP8 GEMM, bf16 out",
+                   "M": M, "N": N, "K": K, "block": [blk, blk], "activation": "bf16 N(0,1)",
+                   "weight": "N(0,0.02) quantized per [128,128] tile", "bias": None},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "paths": paths,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,217 @@
+/*
+ * q8gemm — scaled 8-bit GEMM for LLM linear layers on AMD Instinct MI355X
+ * (gfx950 / CDNA4). C ABI.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument is a DEVICE pointer (hipMalloc'd or a torch CUDA
+ *   tensor's data_ptr), unless a comment says otherwise. The caller owns and
+ *   allocates every buffer, outputs and workspace included; outputs are
+ *   written in place. The library never allocates or frees memory, keeps no
+ *   global state and may be called from several threads at once.
+ * - Every matrix is row-major and contiguous unless a leading dimension is
+ *   passed. Weights are [N, K] with K contiguous (the "nt" layout: a
+ *   column-major [K, N] weight is the same bytes).
+ * - All calls are asynchronous on `stream` (0 = the null stream).
+ * - Return value: Q8_OK (0) or a negative Q8_E* code. Every argument is
+ *   validated on the host before any HIP call, so an invalid call touches
+ *   neither the device nor the stream. q8gemm_last_error() then returns a
+ *   message for the calling thread. Device-side preconditions (for example
+ *   expert ids in range) are documented per call and are not checked.
+ * - FP8 means OCP float8 e4m3fn (torch.float8_e4m3fn): largest finite 448,
+ *   no infinities, codes 0x7F/0xFF are NaN.
+ */
+#ifndef Q8GEMM_H
+#define Q8GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  Q8_OK = 0,
+  Q8_EINVAL = -1,        /* null pointer, bad dtype or enum value          */
+  Q8_ESHAPE = -2,        /* a size or divisibility rule is broken          */
+  Q8_EUNSUPPORTED = -3,  /* a valid request this build does not implement  */
+  Q8_EWORKSPACE = -4,    /* workspace missing or smaller than required     */
+  Q8_EHIP = -5           /* a HIP call (kernel launch) failed              */
+};
+
+typedef enum {
+  Q8_F32 = 0,
+  Q8_BF16 = 1,
+  Q8_F16 = 2,
+  Q8_E4M3FN = 3,
+  Q8_I8 = 4,
+  Q8_I32 = 5
+} q8_dtype;
+
+typedef enum {
+  Q8_SCALE_PER_GROUP = 0,          /* s[M, K/group_size], one per token group */
+  Q8_SCALE_PER_TENSOR_DYNAMIC = 1, /* s[1] from the whole tensor's |max|      */
+  Q8_SCALE_STATIC = 2              /* s[1] is an INPUT scale                  */
+} q8_scale_mode;
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* q8gemm_last_error(void);
+
+/*
+ * 8-bit activation quantization.
+ * "Implementation: Sgl project Sglang GEMM Interface", Description >
+ * Quantization Routines: sgl_per_token_group_quant_8bit (per token, per
+ * group of group_size consecutive K elements, FP8 or INT8, epsilon,
+ * clipping range, optional UE8M0 scale), sgl_per_token_quant_fp8 (one group
+ * per row: group_size = K) and sgl_per_tensor_quant_fp8 (static or dynamic
+ * per-tensor scale); the INT8 flavour is the symmetric dynamic/static
+ * quantization of the vLLM scaled_mm page (AiterInt8ScaledMMLinearKernel).
+ *
+ * x       [M, K] of x_dtype (Q8_F32, Q8_BF16 or Q8_F16), row stride ld_x >= K
+ *         elements.
+ * q       [M, K] of q_dtype (Q8_E4M3FN or Q8_I8), contiguous (row stride K).
+ * s       Q8_SCALE_PER_GROUP: output, [M, K/group_size] float32 row-major.
+ *         Q8_SCALE_PER_TENSOR_DYNAMIC: output, s[0].
+ *         Q8_SCALE_STATIC: input, s[0] (must be > 0; read on the device).
+ * Per group (all float32, round to nearest even):
+ *   a = max|x|; s = max(a, eps) / qmax; UE8M0: s rounded up to a power of
+ *   two; y = clamp(x / s, qmin, qmax) with a true division; FP8: nearest
+ *   e4m3fn code, ties to even, sign kept (-0 -> 0x80); INT8: rint(y).
+ * group_size must divide K (PER_GROUP); it is ignored by the other modes.
+ * eps > 0 floors a (an all-zero group gets s = eps/qmax and zero codes).
+ * Typical ranges: FP8 qmin=-448, qmax=448; INT8 qmin=-128, qmax=127.
+ * scale_ue8m0 must be 0 with Q8_SCALE_STATIC.
+ * fuse_silu_and_mul must be 0 and masked_m NULL (not implemented:
+ * Q8_EUNSUPPORTED).
+ * workspace: Q8_SCALE_PER_TENSOR_DYNAMIC needs quant_8bit_workspace_size()
+ * bytes (partial maxima); other modes need none (NULL, 0 allowed).
+ * M == 0 or K == 0 is a no-op.
+ */
+size_t quant_8bit_workspace_size(int64_t M, int64_t K, q8_scale_mode mode);
+int quant_8bit(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, int64_t ld_x,
+               void* q, q8_dtype q_dtype, float* s, int64_t group_size,
+               q8_scale_mode mode, float eps, float qmin, float qmax,
+               int scale_ue8m0, int fuse_silu_and_mul, const int32_t* masked_m,
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Block-scaled FP8 GEMM with bf16/f16 output.
+ * The block32 DeepGEMM PR for DeepSeek-V4.1 ("[SM90] Use native block32
+ * DeepGEMM for DeepSeek-V4.1"), Modifications: fp8_gemm_nt((Aq, As), (Wq, Ws),
+ * D, recipe=(1, bn, bk)) with [32,32] or [128,128] weight blocks; weight
+ * scale layout [n_blocks, k_blocks] from the vLLM scaled_mm page
+ * (XPUFp8BlockScaledMMKernel).
+ *
+ *   D[m,n] = sum_kb As[m,kb] * Ws[n/bn, kb] * sum_{k in kb} A[m,k] * W[n,k]
+ *            (+ bias[n]), rounded to nearest even into out_dtype.
+ *
+ * A   [M, K] e4m3fn, As [M, K/bk] float32 (activation groups of 1 x bk).
+ * W   [N, K] e4m3fn, Ws [ceil(N/bn), K/bk] float32.
+ * bias [N] of out_dtype, or NULL.   D [M, N] of out_dtype (Q8_BF16, Q8_F16).
+ * Rules: bk in {32, 128}; bn a positive multiple of 16; K % bk == 0
+ * (ragged K is rejected, as the vLLM XPU kernel does); any M >= 0, N >= 1.
+ * Accumulation: FP8 products summed in float32 per K block, scaled and
+ * summed in float32.
+ * workspace: blockwise_scaled_mm_workspace_size() bytes (0 today; reserved
+ * for split-K partials).
+ */
+size_t blockwise_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K, int bn, int bk);
+int blockwise_scaled_mm(const void* A, const float* As, const void* W, const float* Ws,
+                        const void* bias, void* D, q8_dtype out_dtype,
+                        int64_t M, int64_t N, int64_t K, int bn, int bk,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * INT8 W8A8 scaled GEMM.
+ * vLLM scaled_mm page, AiterInt8ScaledMMLinearKernel.apply_weights: output =
+ * mm(scale_a * a, scale_b * b) with numpy-style broadcasting, weights [N, K],
+ * N and K multiples of 16, bias [N] of the output dtype; "Implementation: Sgl
+ * project Sglang GEMM Interface", int8_scaled_mm (scales and optional bias).
+ *
+ * A [M, K] int8, W [N, K] int8. acc[m,n] = sum_k A[m,k] * W[n,k] in int32
+ * (exact: |acc| <= 128*128*K < 2^31 for K <= 131071).
+ * out_dtype Q8_BF16 / Q8_F16: D = ((float)acc * sa[m or 0]) * sb[n or 0]
+ *   (+ (float)bias[n]) in float32 without contraction, then RNE.
+ *   sa_numel in {1, M}, sb_numel in {1, N}; all four combinations broadcast.
+ * out_dtype Q8_I32: D receives acc itself; sa, sb and bias must be NULL.
+ * Rules: N % 16 == 0, K % 16 == 0, K <= 131071.
+ */
+int scaled_mm_int8(const int8_t* A, const float* sa, int64_t sa_numel,
+                   const int8_t* W, const float* sb, int64_t sb_numel,
+                   const void* bias, void* D, q8_dtype out_dtype,
+                   int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * MoE routing tables from the router's top-k expert ids.
+ * "Implementation: Sgl project Sglang CUTLASS MoE", Description and I/O
+ * Contract (get_cutlass_w4a8_moe_mm_data): expert offsets, per-expert problem
+ * sizes, and the input/output permutations around the grouped GEMM.
+ *
+ * topk_ids [T, topk] int32, values in [0, E) (device precondition).
+ * With flat index i = t * topk + j:
+ *   expert_offsets [E+1]: exclusive prefix sum of the per-expert counts,
+ *                         expert_offsets[E] = T * topk;
+ *   problem_sizes1 [E, 3] = (m_e, n, k); problem_sizes2 [E, 3] = (m_e, k, n);
+ *   input_permutation  [T*topk]: token row feeding sorted slot p;
+ *   output_permutation [T*topk]: sorted slot holding flat choice i.
+ * Within one expert, slots follow ascending flat index (stable), so the
+ * result is deterministic and unique.
+ * Rules: T >= 0, 1 <= topk, 1 <= E <= 1024, T * topk < 2^31.
+ * workspace: moe_mm_data_workspace_size() bytes.
+ */
+size_t moe_mm_data_workspace_size(int64_t T, int topk, int E);
+int moe_mm_data(const int32_t* topk_ids, int64_t T, int topk, int E, int64_t n, int64_t k,
+                int32_t* expert_offsets, int32_t* problem_sizes1, int32_t* problem_sizes2,
+                int32_t* input_permutation, int32_t* output_permutation,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Expert-grouped block-scaled FP8 GEMM.
+ * "Implementation: Sgl project Sglang CUTLASS MoE" (cutlass_w4a8_moe_mm:
+ * grouped GEMM over expert segments given by expert_offsets and
+ * problem_sizes), here with FP8 weights in [bn, bk] blocks as in
+ * blockwise_scaled_mm.
+ *
+ * For each expert e and sorted slot p in [expert_offsets[e], expert_offsets[e+1]):
+ *   row(p) = a_map ? a_map[p] : p            (fused input gather)
+ *   Dsorted[p, :] = blockwise(A[row(p)], As[row(p)], W[e], Ws[e])
+ * and Dsorted[p] is stored at D row p when c_map is NULL, otherwise at every
+ * row i with c_map[i] == p — pass output_permutation to un-permute into the
+ * [T*topk, N] order of the flat choices (fused output scatter; c_map must be
+ * a permutation of [0, total_m), and the library uses its inverse, so
+ * c_map's row count must equal total_m).
+ * A [*, K] e4m3fn (rows addressed through a_map), As [*, K/bk] float32,
+ * W [E, N, K] e4m3fn, Ws [E, ceil(N/bn), K/bk] float32, D [total_m, N].
+ * problem_sizes [E, 3] (m_e, N, K) must agree with expert_offsets (device
+ * precondition; the kernels take the row ranges from expert_offsets).
+ * Rules as blockwise_scaled_mm; total_m = expert_offsets[E] (host value).
+ * workspace: grouped_blockwise_scaled_mm_workspace_size() bytes (the inverse
+ * of c_map).
+ */
+size_t grouped_blockwise_scaled_mm_workspace_size(int E, int64_t total_m, int64_t N, int64_t K,
+                                                  int bn, int bk);
+int grouped_blockwise_scaled_mm(const void* A, const float* As, const void* W, const float* Ws,
+                                void* D, q8_dtype out_dtype,
+                                const int32_t* expert_offsets, const int32_t* problem_sizes,
+                                const int32_t* a_map, const int32_t* c_map,
+                                int E, int64_t total_m, int64_t N, int64_t K, int bn, int bk,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Row gather.
+ * "Implementation: Sgl project Sglang GEMM Interface", Utility: shuffle_rows
+ * (permute rows by a destination-to-source map).
+ * dst[i, :] = src[dst2src[i], :] for 0 <= i < dst_rows; rows are row_bytes
+ * bytes (any dtype). dst2src values must index valid src rows (device
+ * precondition). src and dst must not overlap.
+ */
+int shuffle_rows(const void* src, int64_t row_bytes, const int32_t* dst2src, int64_t dst_rows,
+                 void* dst, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8GEMM_H */

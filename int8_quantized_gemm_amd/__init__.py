@@ -1,0 +1,278 @@
+"""Python binding of libq8gemm (scaled 8-bit GEMM for MI355X / gfx950).
+
+Argument marshalling only: each function checks that torch tensors are on the
+GPU and laid out as the C ABI expects (``include/q8gemm.h``), then passes raw
+pointers, sizes and the current HIP stream to the library. Every step of the
+computation runs in the library's HIP kernels; there is no fallback, and
+importing this package fails loudly when ``libq8gemm.so`` is missing (build it
+with ``python -m int8_quantized_gemm_amd.build``).
+
+Names and argument orders follow the pages' wrappers: sgl-kernel's
+``sgl_per_token_group_quant_8bit``, ``fp8_blockwise_scaled_mm``,
+``int8_scaled_mm`` and ``shuffle_rows`` ("Implementation: Sgl project Sglang
+GEMM Interface", Signature), and ``get_cutlass_w4a8_moe_mm_data`` /
+``cutlass_w4a8_moe_mm`` ("Implementation: Sgl project Sglang CUTLASS MoE",
+Signature).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libq8gemm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m int8_quantized_gemm_amd.build` "
+        "(there is no CPU fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# status codes and enums of include/q8gemm.h
+Q8_OK, Q8_EINVAL, Q8_ESHAPE, Q8_EUNSUPPORTED, Q8_EWORKSPACE, Q8_EHIP = 0, -1, -2, -3, -4, -5
+Q8_F32, Q8_BF16, Q8_F16, Q8_E4M3FN, Q8_I8, Q8_I32 = 0, 1, 2, 3, 4, 5
+SCALE_PER_GROUP, SCALE_PER_TENSOR_DYNAMIC, SCALE_STATIC = 0, 1, 2
+
+EXPORTS = (
+    "q8gemm_last_error",
+    "quant_8bit_workspace_size", "quant_8bit",
+    "blockwise_scaled_mm_workspace_size", "blockwise_scaled_mm",
+    "scaled_mm_int8",
+    "moe_mm_data_workspace_size", "moe_mm_data",
+    "grouped_blockwise_scaled_mm_workspace_size", "grouped_blockwise_scaled_mm",
+    "shuffle_rows",
+)
+
+_p, _i64, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+def _sig(name, res, *args):
+    fn = getattr(_lib, name)
+    fn.restype = res
+    fn.argtypes = list(args)
+    return fn
+
+
+_lib_last_error = _sig("q8gemm_last_error", ctypes.c_char_p)
+_quant_ws = _sig("quant_8bit_workspace_size", _sz, _i64, _i64, _i)
+_quant = _sig("quant_8bit", _i, _p, _i, _i64, _i64, _i64, _p, _i, _p, _i64, _i, _f, _f, _f, _i, _i,
+              _p, _p, _sz, _p)
+_bmm_ws = _sig("blockwise_scaled_mm_workspace_size", _sz, _i64, _i64, _i64, _i, _i)
+_bmm = _sig("blockwise_scaled_mm", _i, _p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i, _i, _p,
+            _sz, _p)
+_imm = _sig("scaled_mm_int8", _i, _p, _p, _i64, _p, _p, _i64, _p, _p, _i, _i64, _i64, _i64, _p)
+_moe_ws = _sig("moe_mm_data_workspace_size", _sz, _i64, _i, _i)
+_moe = _sig("moe_mm_data", _i, _p, _i64, _i, _i, _i64, _i64, _p, _p, _p, _p, _p, _p, _sz, _p)
+_gmm_ws = _sig("grouped_blockwise_scaled_mm_workspace_size", _sz, _i, _i64, _i64, _i64, _i, _i)
+_gmm = _sig("grouped_blockwise_scaled_mm", _i, _p, _p, _p, _p, _p, _i, _p, _p, _p, _p, _i, _i64,
+            _i64, _i64, _i, _i, _p, _sz, _p)
+_shuf = _sig("shuffle_rows", _i, _p, _i64, _p, _i64, _p, _p)
+
+
+class Q8Error(RuntimeError):
+    """A library call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[status {status}] {message}")
+        self.status = status
+
+
+def last_error() -> str:
+    return _lib_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != Q8_OK:
+        raise Q8Error(status, last_error())
+
+
+_DT = {
+    torch.float32: Q8_F32, torch.bfloat16: Q8_BF16, torch.float16: Q8_F16,
+    torch.float8_e4m3fn: Q8_E4M3FN, torch.uint8: Q8_E4M3FN, torch.int8: Q8_I8,
+    torch.int32: Q8_I32,
+}
+
+
+def _dt(t: torch.dtype) -> int:
+    if t not in _DT:
+        raise TypeError(f"unsupported dtype {t}")
+    return _DT[t]
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(*ts) -> torch.device:
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("every tensor must be on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors on different devices")
+    return dev
+
+
+def _contig(*ts) -> None:
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(dev, nbytes: int):
+    """Device workspace cached per (device, stream); grows, never shrinks."""
+    if nbytes == 0:
+        return None, 0
+    key = (dev, _stream(dev))
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        _ws_cache[key] = buf
+    return buf.data_ptr(), buf.numel()
+
+
+# ---------------------------------------------------------------------------
+def quant_8bit(input: torch.Tensor, output_q: torch.Tensor, output_s: torch.Tensor,
+               group_size: int, eps: float = 1e-10, fp8_min: float = -448.0,
+               fp8_max: float = 448.0, scale_ue8m0: bool = False, mode: int = SCALE_PER_GROUP,
+               fuse_silu_and_mul: bool = False, masked_m: torch.Tensor | None = None) -> None:
+    """Per-token-group (or per-tensor) 8-bit quantization, in place.
+
+    ``input`` [M, K] (fp32/bf16/f16, unit column stride), ``output_q`` [M, K]
+    float8_e4m3fn/uint8 codes or int8, ``output_s`` [M, K // group_size]
+    float32 (``[1]`` for the per-tensor modes; an input for SCALE_STATIC).
+    For INT8 pass ``fp8_min=-128, fp8_max=127``.
+    """
+    dev = _dev(input, output_q, output_s, masked_m)
+    if input.dim() != 2 or input.stride(1) != 1:
+        raise ValueError("input must be 2-D with unit column stride")
+    _contig(output_q, output_s)
+    M, K = input.shape
+    if tuple(output_q.shape) != (M, K):
+        raise ValueError("output_q must have the input's shape")
+    ws, wsb = _workspace(dev, _quant_ws(M, K, mode))
+    _check(_quant(_ptr(input), _dt(input.dtype), M, K, input.stride(0) if M > 1 else K,
+                  _ptr(output_q), _dt(output_q.dtype), _ptr(output_s), group_size, mode, eps,
+                  fp8_min, fp8_max, int(scale_ue8m0), int(fuse_silu_and_mul), _ptr(masked_m),
+                  ws, wsb, _stream(dev)))
+
+
+def blockwise_scaled_mm(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torch.Tensor,
+                        scales_b: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                        bias: torch.Tensor | None = None, block=(128, 128),
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """Block-scaled FP8 GEMM ``D = A @ W.T`` with per-(row, K block) ``scales_a``
+    [M, K/bk] and per-(bn x bk tile) ``scales_b`` [ceil(N/bn), K/bk]."""
+    dev = _dev(mat_a, mat_b, scales_a, scales_b, bias, out)
+    _contig(mat_a, mat_b, scales_a, scales_b, bias)
+    M, K = mat_a.shape
+    N = mat_b.shape[0]
+    if mat_b.shape[1] != K:
+        raise ValueError("mat_b must be [N, K]")
+    bn, bk = block
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    _contig(out)
+    ws, wsb = _workspace(dev, _bmm_ws(M, N, K, bn, bk))
+    _check(_bmm(_ptr(mat_a), _ptr(scales_a), _ptr(mat_b), _ptr(scales_b), _ptr(bias), _ptr(out),
+                _dt(out.dtype), M, N, K, bn, bk, ws, wsb, _stream(dev)))
+    return out
+
+
+def scaled_mm_int8(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torch.Tensor | None,
+                   scales_b: torch.Tensor | None, out_dtype: torch.dtype = torch.bfloat16,
+                   bias: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """INT8 W8A8: ``mat_a`` [M, K] int8; ``mat_b`` [N, K] int8 (or its ``.t()``
+    view [K, N]); ``out_dtype=torch.int32`` returns the raw accumulators."""
+    dev = _dev(mat_a, mat_b, scales_a, scales_b, bias, out)
+    _contig(mat_a, scales_a, scales_b, bias)
+    M, K = mat_a.shape
+    if mat_b.is_contiguous() and mat_b.shape[1] == K:
+        N = mat_b.shape[0]
+    elif mat_b.shape[0] == K and mat_b.stride() == (1, K):
+        N = mat_b.shape[1]  # transposed view of a contiguous [N, K]
+    else:
+        raise ValueError("mat_b must be [N, K] contiguous or the .t() view of one")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    _contig(out)
+    _check(_imm(_ptr(mat_a), _ptr(scales_a), 0 if scales_a is None else scales_a.numel(),
+                _ptr(mat_b), _ptr(scales_b), 0 if scales_b is None else scales_b.numel(),
+                _ptr(bias), _ptr(out), _dt(out.dtype), M, N, K, _stream(dev)))
+    return out
+
+
+def moe_mm_data(topk_ids: torch.Tensor, expert_offsets: torch.Tensor,
+                problem_sizes1: torch.Tensor, problem_sizes2: torch.Tensor,
+                input_permutation: torch.Tensor, output_permutation: torch.Tensor,
+                num_experts: int, n: int, k: int) -> None:
+    """MoE routing tables from ``topk_ids`` [T, topk] int32, in place."""
+    dev = _dev(topk_ids, expert_offsets, problem_sizes1, problem_sizes2, input_permutation,
+               output_permutation)
+    _contig(topk_ids, expert_offsets, problem_sizes1, problem_sizes2, input_permutation,
+            output_permutation)
+    for t in (topk_ids, expert_offsets, problem_sizes1, problem_sizes2, input_permutation,
+              output_permutation):
+        if t.dtype != torch.int32:
+            raise TypeError("routing tensors are int32")
+    T, topk = topk_ids.shape
+    if expert_offsets.numel() < num_experts + 1 or problem_sizes1.numel() < 3 * num_experts \
+            or problem_sizes2.numel() < 3 * num_experts \
+            or input_permutation.numel() < T * topk or output_permutation.numel() < T * topk:
+        raise ValueError("an output tensor is too small")
+    ws, wsb = _workspace(dev, _moe_ws(T, topk, num_experts))
+    _check(_moe(_ptr(topk_ids), T, topk, num_experts, n, k, _ptr(expert_offsets),
+                _ptr(problem_sizes1), _ptr(problem_sizes2), _ptr(input_permutation),
+                _ptr(output_permutation), ws, wsb, _stream(dev)))
+
+
+def grouped_blockwise_scaled_mm(d: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
+                                a_scales: torch.Tensor, b_scales: torch.Tensor,
+                                expert_offsets: torch.Tensor, problem_sizes: torch.Tensor,
+                                a_map: torch.Tensor | None = None,
+                                c_map: torch.Tensor | None = None, block=(128, 128)) -> None:
+    """Expert-grouped block-FP8 GEMM into ``d`` [total_m, N] (in place).
+
+    ``b`` [E, N, K] e4m3fn, ``b_scales`` [E, ceil(N/bn), K/bk]; ``a``/``a_scales``
+    rows are addressed through ``a_map`` (input_permutation) when given;
+    ``c_map`` (output_permutation) un-permutes the result rows.
+    """
+    dev = _dev(d, a, b, a_scales, b_scales, expert_offsets, problem_sizes, a_map, c_map)
+    _contig(d, a, b, a_scales, b_scales, expert_offsets, problem_sizes, a_map, c_map)
+    E, N, K = b.shape
+    total_m = d.shape[0]
+    if d.shape[1] != N or a.shape[1] != K:
+        raise ValueError("shape mismatch")
+    bn, bk = block
+    ws, wsb = _workspace(dev, _gmm_ws(E, total_m, N, K, bn, bk) if c_map is not None else 0)
+    _check(_gmm(_ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales), _ptr(d), _dt(d.dtype),
+                _ptr(expert_offsets), _ptr(problem_sizes), _ptr(a_map), _ptr(c_map), E, total_m,
+                N, K, bn, bk, ws, wsb, _stream(dev)))
+
+
+def shuffle_rows(input_tensor: torch.Tensor, dst2src_map: torch.Tensor,
+                 output_tensor_shape) -> torch.Tensor:
+    """``out[i] = input_tensor[dst2src_map[i]]`` for a row-major tensor."""
+    dev = _dev(input_tensor, dst2src_map)
+    _contig(input_tensor, dst2src_map)
+    out = torch.empty(output_tensor_shape, dtype=input_tensor.dtype, device=dev)
+    rows = dst2src_map.numel()
+    row_bytes = input_tensor[0].numel() * input_tensor.element_size() if input_tensor.shape[0] else 0
+    if out.numel() * out.element_size() != rows * row_bytes:
+        raise ValueError("output shape does not match the map")
+    _check(_shuf(_ptr(input_tensor), row_bytes, _ptr(dst2src_map), rows, _ptr(out), _stream(dev)))
+    return out

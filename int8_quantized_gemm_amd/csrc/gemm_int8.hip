@@ -1,0 +1,181 @@
+// INT8 W8A8 scaled GEMM for gfx950.
+//
+// vLLM scaled_mm page, AiterInt8ScaledMMLinearKernel.apply_weights: output =
+// mm(scale_a * a, scale_b * b) with numpy broadcasting, a [M, K], weights
+// [N, K]; per-tensor x per-tensor and per-token x per-channel scales (the
+// other two combinations broadcast the same way here).
+//
+// The int32 accumulator is exact, so the whole K loop accumulates inside the
+// matrix cores (v_mfma_i32_16x16x64_i8, chained), with no per-block work; the
+// scales and bias are applied once in the epilogue in float32 without FMA
+// contraction: ((float)acc * sa) * sb + bias, then round to nearest even.
+// Tiling, LDS layout and tile order are those of the FP8 tile kernel.
+#include "q8_internal.h"
+#include "tile_common.h"
+
+namespace q8 {
+namespace {
+
+struct Int8Params {
+  const int8_t* A;
+  const float* sa;
+  const int8_t* W;
+  const float* sb;
+  const void* bias;
+  void* D;
+  int64_t M, N, K;
+  int sa_per_row, sb_per_col;
+  int out_kind;  // 0 = int32, 1 = bf16, 2 = f16
+  int64_t tiles_m, tiles_n;
+};
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_int8_tile(Int8Params p) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int A_CH = BM * 8 / NT, B_CH = BN * 8 / NT;
+  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/thread mismatch");
+
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * 128];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WN, wn = wid % WN;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t M = p.M, N = p.N, K = p.K;
+
+  const int64_t t = xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n);
+  int64_t tm, tn;
+  grouped_order(t, p.tiles_m, p.tiles_n, 8, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+
+  const int8_t* a_src[A_CH];
+  const int8_t* b_src[B_CH];
+#pragma unroll
+  for (int c = 0; c < A_CH; ++c) {
+    const int idx = tid + c * NT, r = idx >> 3, ch = idx & 7;
+    const int64_t m = m0 + r < M ? m0 + r : M - 1;
+    a_src[c] = p.A + m * K + ch * 16;
+  }
+#pragma unroll
+  for (int c = 0; c < B_CH; ++c) {
+    const int idx = tid + c * NT, r = idx >> 3, ch = idx & 7;
+    const int64_t n = n0 + r < N ? n0 + r : N - 1;
+    b_src[c] = p.W + n * K + ch * 16;
+  }
+
+  uint4 ra[A_CH], rb[B_CH];
+  // K is a multiple of 16 but not necessarily of 128: the last slab reads
+  // only the chunks below K and zero-fills the rest.
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      const int ch = (tid + c * NT) & 7;
+      ra[c] = k0 + ch * 16 < K ? *reinterpret_cast<const uint4*>(a_src[c] + k0) : uint4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int c = 0; c < B_CH; ++c) {
+      const int ch = (tid + c * NT) & 7;
+      rb[c] = k0 + ch * 16 < K ? *reinterpret_cast<const uint4*>(b_src[c] + k0) : uint4{0, 0, 0, 0};
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      const int idx = tid + c * NT;
+      *reinterpret_cast<uint4*>(&sA[buf][swz(idx >> 3, idx & 7)]) = ra[c];
+    }
+#pragma unroll
+    for (int c = 0; c < B_CH; ++c) {
+      const int idx = tid + c * NT;
+      *reinterpret_cast<uint4*>(&sB[buf][swz(idx >> 3, idx & 7)]) = rb[c];
+    }
+  };
+
+  i32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+
+  const int KT = (int)((K + 127) / 128);
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload((int64_t)(kt + 1) * 128);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      i32x4 bf[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bf[j] = *reinterpret_cast<const i32x4*>(&sB[buf][swz(wn * TN + j * 16 + r16, 4 * h + g)]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const i32x4 af = *reinterpret_cast<const i32x4*>(&sA[buf][swz(wm * TM + i * 16 + r16, 4 * h + g)]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < KT) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int64_t col = n0 + wn * TN + j * 16 + r16;
+    if (col >= N) continue;
+    float sbv = 0.f, bv = 0.f;
+    if (p.out_kind != 0) {
+      sbv = p.sb[p.sb_per_col ? col : 0];
+      if (p.bias) {
+        const uint16_t h = static_cast<const uint16_t*>(p.bias)[col];
+        bv = p.out_kind == 1 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int64_t row = m0 + wm * TM + i * 16 + 4 * g + rr;
+        if (row >= M) continue;
+        const int v = acc[i][j][rr];
+        if (p.out_kind == 0) {
+          static_cast<int32_t*>(p.D)[row * N + col] = v;
+        } else {
+          const float sav = p.sa[p.sa_per_row ? row : 0];
+          float o = __fmul_rn(__fmul_rn((float)v, sav), sbv);
+          if (p.bias) o = __fadd_rn(o, bv);
+          static_cast<uint16_t*>(p.D)[row * N + col] =
+              (uint16_t)(p.out_kind == 1 ? f32_to_bf16_bits(o) : f32_to_f16_bits(o));
+        }
+      }
+    }
+  }
+}
+
+constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 4;
+
+}  // namespace
+
+hipError_t launch_int8(const Int8GemmArgs& a, hipStream_t st) {
+  if (a.M == 0) return hipSuccess;
+  Int8Params p{};
+  p.A = a.A; p.sa = a.sa; p.W = a.W; p.sb = a.sb; p.bias = a.bias; p.D = a.D;
+  p.M = a.M; p.N = a.N; p.K = a.K;
+  p.sa_per_row = a.sa_numel > 1 || (a.sa_numel == a.M && a.M == 1);
+  p.sb_per_col = a.sb_numel > 1 || (a.sb_numel == a.N && a.N == 1);
+  p.out_kind = a.out_dtype == Q8_I32 ? 0 : (a.out_dtype == Q8_BF16 ? 1 : 2);
+  p.tiles_m = (a.M + kBM - 1) / kBM;
+  p.tiles_n = (a.N + kBN - 1) / kBN;
+  const int64_t tiles = p.tiles_m * p.tiles_n;
+  if (tiles > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((gemm_int8_tile<kBM, kBN, kWM, kWN>), dim3((unsigned)tiles),
+                     dim3(kWM * kWN * 64), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace q8

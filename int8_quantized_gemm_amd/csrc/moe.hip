@@ -1,0 +1,163 @@
+// MoE routing-table construction and row gather for gfx950.
+//
+// "Implementation: Sgl project Sglang CUTLASS MoE", Description: from the
+// router's topk_ids build expert_offsets, per-expert problem sizes and the
+// input/output permutations around the grouped GEMM; "Implementation: Sgl
+// project Sglang GEMM Interface", Utility: shuffle_rows (destination-to-
+// source row permutation).
+//
+// Routing is a stable counting sort over the flat choices i = t*topk + j:
+//   1. moe_count  — one workgroup per chunk of 256 flat entries builds the
+//                   chunk's per-expert histogram in LDS (counts are order
+//                   independent);
+//   2. moe_scan   — one thread per expert scans its counts over the chunks
+//                   (exclusive), then the per-expert totals are scanned over
+//                   the experts into expert_offsets and problem sizes, and the
+//                   chunk bases are shifted by the expert offsets;
+//   3. moe_scatter — each entry's slot = its chunk's base for its expert plus
+//                   the number of earlier entries of the same expert inside
+//                   the chunk (counted from an LDS copy of the chunk), so
+//                   slots ascend with the flat index inside every expert and
+//                   the tables are deterministic.
+#include "q8_internal.h"
+#include "q8_device.h"
+
+namespace q8 {
+namespace {
+
+constexpr int kChunk = 256;
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kChunk) void moe_count(const int32_t* __restrict__ ids, int64_t n,
+                                                    int E, int32_t* __restrict__ counts) {
+  extern __shared__ int32_t hist[];
+  for (int e = threadIdx.x; e < E; e += kChunk) hist[e] = 0;
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * kChunk + threadIdx.x;
+  if (i < n) atomicAdd(&hist[ids[i]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kChunk) counts[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+__global__ __launch_bounds__(kScanThreads) void moe_scan(int32_t* __restrict__ counts,
+                                                         int64_t nchunks, int E, int64_t nk,
+                                                         int64_t kk, int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ ps1,
+                                                         int32_t* __restrict__ ps2) {
+  __shared__ int32_t tot[kScanThreads];
+  const int e = threadIdx.x;
+  int32_t run = 0;
+  if (e < E) {
+    for (int64_t c = 0; c < nchunks; ++c) {
+      const int32_t v = counts[c * E + e];
+      counts[c * E + e] = run;
+      run += v;
+    }
+  }
+  tot[e] = e < E ? run : 0;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over the per-expert totals
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const int32_t v = e >= off ? tot[e - off] : 0;
+    __syncthreads();
+    tot[e] += v;
+    __syncthreads();
+  }
+  if (e < E) {
+    const int32_t base = tot[e] - run;  // exclusive prefix
+    offsets[e] = base;
+    if (e == E - 1) offsets[E] = tot[e];
+    ps1[3 * e + 0] = run; ps1[3 * e + 1] = (int32_t)nk; ps1[3 * e + 2] = (int32_t)kk;
+    ps2[3 * e + 0] = run; ps2[3 * e + 1] = (int32_t)kk; ps2[3 * e + 2] = (int32_t)nk;
+    for (int64_t c = 0; c < nchunks; ++c) counts[c * E + e] += base;
+  }
+}
+
+__global__ __launch_bounds__(kChunk) void moe_scatter(const int32_t* __restrict__ ids, int64_t n,
+                                                      int topk, int E,
+                                                      const int32_t* __restrict__ bases,
+                                                      int32_t* __restrict__ in_perm,
+                                                      int32_t* __restrict__ out_perm) {
+  __shared__ int32_t sid[kChunk];
+  const int64_t i0 = (int64_t)blockIdx.x * kChunk;
+  const int64_t i = i0 + threadIdx.x;
+  const int32_t id = i < n ? ids[i] : -1;
+  sid[threadIdx.x] = id;
+  __syncthreads();
+  if (i >= n) return;
+  int32_t rank = 0;
+  for (int t = 0; t < (int)threadIdx.x; ++t) rank += sid[t] == id;
+  const int32_t slot = bases[(int64_t)blockIdx.x * E + id] + rank;
+  in_perm[slot] = (int32_t)(i / topk);
+  out_perm[i] = slot;
+}
+
+__global__ void shuffle_rows_vec(const uint4* __restrict__ src, int64_t row_vecs,
+                                 const int32_t* __restrict__ map, int64_t rows,
+                                 uint4* __restrict__ dst) {
+  const int64_t total = rows * row_vecs;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total;
+       v += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = v / row_vecs, c = v - r * row_vecs;
+    dst[v] = src[(int64_t)map[r] * row_vecs + c];
+  }
+}
+
+__global__ void shuffle_rows_bytes(const uint8_t* __restrict__ src, int64_t row_bytes,
+                                   const int32_t* __restrict__ map, int64_t rows,
+                                   uint8_t* __restrict__ dst) {
+  const int64_t total = rows * row_bytes;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total;
+       v += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = v / row_bytes, c = v - r * row_bytes;
+    dst[v] = src[(int64_t)map[r] * row_bytes + c];
+  }
+}
+
+}  // namespace
+
+size_t moe_workspace_ints(int64_t T, int topk, int E) {
+  const int64_t n = T * topk;
+  const int64_t nchunks = (n + kChunk - 1) / kChunk;
+  return (size_t)(nchunks * E);
+}
+
+hipError_t launch_moe_mm_data(const int32_t* ids, int64_t T, int topk, int E, int64_t nk,
+                              int64_t kk, int32_t* offsets, int32_t* ps1, int32_t* ps2,
+                              int32_t* in_perm, int32_t* out_perm, int32_t* ws,
+                              hipStream_t st) {
+  const int64_t n = T * topk;
+  const int64_t nchunks = (n + kChunk - 1) / kChunk;
+  if (nchunks > 0) {
+    hipLaunchKernelGGL(moe_count, dim3((unsigned)nchunks), dim3(kChunk), E * sizeof(int32_t), st,
+                       ids, n, E, ws);
+  }
+  hipLaunchKernelGGL(moe_scan, dim3(1), dim3(kScanThreads), 0, st, ws, nchunks, E, nk, kk,
+                     offsets, ps1, ps2);
+  if (nchunks > 0) {
+    hipLaunchKernelGGL(moe_scatter, dim3((unsigned)nchunks), dim3(kChunk), 0, st, ids, n, topk,
+                       E, ws, in_perm, out_perm);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_shuffle_rows(const void* src, int64_t row_bytes, const int32_t* map,
+                               int64_t rows, void* dst, hipStream_t st) {
+  if (rows == 0 || row_bytes == 0) return hipSuccess;
+  const int threads = 256;
+  const bool vec = row_bytes % 16 == 0 && (uintptr_t)src % 16 == 0 && (uintptr_t)dst % 16 == 0;
+  const int64_t work = vec ? rows * (row_bytes / 16) : rows * row_bytes;
+  int64_t blocks = (work + threads - 1) / threads;
+  if (blocks > 65536) blocks = 65536;
+  if (vec)
+    hipLaunchKernelGGL(shuffle_rows_vec, dim3((unsigned)blocks), dim3(threads), 0, st,
+                       static_cast<const uint4*>(src), row_bytes / 16, map, rows,
+                       static_cast<uint4*>(dst));
+  else
+    hipLaunchKernelGGL(shuffle_rows_bytes, dim3((unsigned)blocks), dim3(threads), 0, st,
+                       static_cast<const uint8_t*>(src), row_bytes, map, rows,
+                       static_cast<uint8_t*>(dst));
+  return hipGetLastError();
+}
+
+}  // namespace q8

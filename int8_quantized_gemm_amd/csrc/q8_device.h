@@ -1,0 +1,66 @@
+// Device-side helpers shared by the gfx950 kernels of this library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8 {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// ---- 16-bit float <-> float32 (bit exact, no library dependency) -----------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)h);
+  return (float)v;
+}
+
+// float32 -> bf16 bits, round to nearest even (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;  // v_cvt_f16_f32: round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+// Output element store helper: OUT_BF16 selects bf16, otherwise f16.
+template <bool OUT_BF16>
+__device__ __forceinline__ uint32_t f32_to_out_bits(float f) {
+  if constexpr (OUT_BF16) return f32_to_bf16_bits(f);
+  else return f32_to_f16_bits(f);
+}
+
+template <bool OUT_BF16>
+__device__ __forceinline__ float out_bits_to_f32(uint32_t h) {
+  if constexpr (OUT_BF16) return bf16_bits_to_f32(h);
+  else return f16_bits_to_f32(h);
+}
+
+// ---- wave reductions ----------------------------------------------------------
+__device__ __forceinline__ float wave_max_xor(float v, int width) {
+  for (int off = width >> 1; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// Round a positive float32 up to a power of two (bitwise; powers of two unchanged).
+__device__ __forceinline__ float ue8m0_ceil(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u & 0x007FFFFFu) u = (u & 0x7F800000u) + 0x00800000u;
+  return __uint_as_float(u);
+}
+
+}  // namespace q8

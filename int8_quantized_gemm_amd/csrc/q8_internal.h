@@ -1,0 +1,58 @@
+// Internal declarations shared by the C-ABI front end (capi.cpp) and the
+// kernel translation units. Launchers assume their arguments were validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/q8gemm.h"
+
+namespace q8 {
+
+// ---- quantization -----------------------------------------------------------
+struct QuantArgs {
+  const void* x; q8_dtype x_dtype; int64_t M, K, ld_x;
+  void* q; q8_dtype q_dtype; float* s; int64_t group_size;
+  q8_scale_mode mode; float eps, qmin, qmax; int ue8m0;
+  void* workspace;
+};
+size_t quant_partials_count(int64_t M, int64_t K);
+hipError_t launch_quant(const QuantArgs& a, hipStream_t stream);
+
+// ---- block-scaled FP8 GEMM --------------------------------------------------
+struct BlockGemmArgs {
+  const uint8_t* A; const float* As; const uint8_t* W; const float* Ws;
+  const void* bias; void* D; q8_dtype out_dtype;
+  int64_t M, N, K; int bn, bk;
+  // grouped / MoE extensions (null for the dense call)
+  const int32_t* expert_offsets;  // [E+1]
+  const int32_t* a_map;           // sorted slot -> A row
+  const int32_t* c_inv;           // sorted slot -> D row
+  int E;
+  int64_t w_expert_stride;        // bytes between experts in W
+  int64_t ws_expert_stride;       // floats between experts in Ws
+};
+hipError_t launch_blockwise(const BlockGemmArgs& a, hipStream_t stream);
+hipError_t launch_grouped(const BlockGemmArgs& a, int64_t total_m, int32_t* c_inv_ws,
+                          const int32_t* c_map, hipStream_t stream);
+
+// ---- INT8 GEMM ----------------------------------------------------------------
+struct Int8GemmArgs {
+  const int8_t* A; const float* sa; int64_t sa_numel;
+  const int8_t* W; const float* sb; int64_t sb_numel;
+  const void* bias; void* D; q8_dtype out_dtype;
+  int64_t M, N, K;
+};
+hipError_t launch_int8(const Int8GemmArgs& a, hipStream_t stream);
+
+// ---- MoE routing + row gather -------------------------------------------------
+size_t moe_workspace_ints(int64_t T, int topk, int E);
+hipError_t launch_moe_mm_data(const int32_t* topk_ids, int64_t T, int topk, int E,
+                              int64_t n, int64_t k, int32_t* offsets, int32_t* ps1,
+                              int32_t* ps2, int32_t* in_perm, int32_t* out_perm,
+                              int32_t* ws, hipStream_t stream);
+hipError_t launch_shuffle_rows(const void* src, int64_t row_bytes, const int32_t* dst2src,
+                               int64_t dst_rows, void* dst, hipStream_t stream);
+
+}  // namespace q8

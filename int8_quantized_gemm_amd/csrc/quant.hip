@@ -1,0 +1,350 @@
+// 8-bit activation quantization kernels for gfx950.
+//
+// "Implementation: Sgl project Sglang GEMM Interface", Description >
+// Quantization Routines: per-token-group 8-bit quantization (FP8 e4m3fn or
+// INT8) with epsilon, clipping range and optional UE8M0 scales; per-token
+// (one group per row) and per-tensor (static or dynamic) variants.
+//
+// Per group, in float32 with round-to-nearest-even:
+//   a = max|x|, s = max(a, eps) / qmax, UE8M0: s -> next power of two,
+//   y = clamp(x / s, qmin, qmax), code = e4m3fn(y) (hardware RNE convert) or
+//   rint(y) for INT8.
+// x / s is a true IEEE division (hipcc's default correctly rounded fp32
+// divide); with a power-of-two scale it is done as an exact multiply by 1/s.
+//
+// Kernels
+//   quant_group_wave   groups of 8..512 elements (power of two): each lane
+//                      loads 8 consecutive elements (16 B for bf16/f16), the
+//                      group's lanes are adjacent in one wave and reduce their
+//                      absolute maximum with xor shuffles. HBM-bound.
+//   quant_group_block  any group size (per-token rows, odd sizes, unaligned
+//                      strides): one workgroup per group, block reduction,
+//                      then a second pass that re-reads the group (L2 hit).
+//   amax_partials +    per-tensor dynamic: per-workgroup maxima into the
+//   quant_tensor       workspace, then every workgroup reduces them (the max
+//                      is order independent, so the result is deterministic)
+//                      and quantizes a grid-stride slice. Static mode reads
+//                      the given scale instead.
+#include "q8_internal.h"
+#include "q8_device.h"
+
+namespace q8 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTensorPartials = 512;
+
+// ---- element loads -----------------------------------------------------------
+template <int XT>
+__device__ __forceinline__ void load8(const void* base, int64_t idx, float (&f)[8]) {
+  if constexpr (XT == Q8_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    float4 a = p[0], b = p[1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  } else {
+    const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (XT == Q8_BF16) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      } else {
+        f[2 * i] = f16_bits_to_f32(w[i] & 0xFFFFu);
+        f[2 * i + 1] = f16_bits_to_f32(w[i] >> 16);
+      }
+    }
+  }
+}
+
+template <int XT>
+__device__ __forceinline__ float load1(const void* base, int64_t idx) {
+  if constexpr (XT == Q8_F32) return static_cast<const float*>(base)[idx];
+  else if constexpr (XT == Q8_BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[idx]);
+  else return f16_bits_to_f32(static_cast<const uint16_t*>(base)[idx]);
+}
+
+// ---- scale and codes -----------------------------------------------------------
+template <bool UE>
+__device__ __forceinline__ float group_scale(float amax, float eps, float qmax) {
+  float s = fmaxf(amax, eps) / qmax;
+  return UE ? ue8m0_ceil(s) : s;
+}
+
+// y = clamp(x / s). With UE8M0 the scale is a power of two and x * (1/s) is
+// the same correctly rounded value as x / s whenever 1/s is a normal float
+// (s in [2^-126, 2^126]); outside that range the true division is used.
+template <bool UE>
+struct Divider {
+  float s, inv;
+  bool mul;
+  __device__ __forceinline__ explicit Divider(float s_) : s(s_) {
+    mul = UE && s_ >= 1.17549435e-38f && s_ <= 8.5070592e37f;
+    inv = mul ? 1.0f / s_ : 0.0f;
+  }
+  __device__ __forceinline__ float operator()(float x, float qmin, float qmax) const {
+    float y;
+    if constexpr (UE) y = mul ? x * inv : x / s;
+    else y = x / s;
+    return fminf(fmaxf(y, qmin), qmax);
+  }
+};
+
+template <bool FP8>
+__device__ __forceinline__ uint32_t encode_pair_bytes(float a, float b) {
+  if constexpr (FP8) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+  } else {
+    int ia = (int)__builtin_rintf(a), ib = (int)__builtin_rintf(b);
+    return ((uint32_t)ia & 0xFFu) | (((uint32_t)ib & 0xFFu) << 8);
+  }
+}
+
+template <bool FP8>
+__device__ __forceinline__ uint2 encode8(const float (&y)[8]) {
+  uint2 r;
+  r.x = encode_pair_bytes<FP8>(y[0], y[1]) | (encode_pair_bytes<FP8>(y[2], y[3]) << 16);
+  r.y = encode_pair_bytes<FP8>(y[4], y[5]) | (encode_pair_bytes<FP8>(y[6], y[7]) << 16);
+  return r;
+}
+
+template <bool FP8>
+__device__ __forceinline__ uint8_t encode1(float y) {
+  return (uint8_t)(encode_pair_bytes<FP8>(y, 0.0f) & 0xFFu);
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max_xor(v, kWave);
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / kWave; ++i) r = fmaxf(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+// ---- kernels ---------------------------------------------------------------------
+template <int XT, bool FP8, bool UE, int TPG>
+__global__ __launch_bounds__(kThreads) void quant_group_wave(
+    const void* __restrict__ x, int64_t M, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
+    float* __restrict__ s, float eps, float qmin, float qmax) {
+  const int64_t vpr = K >> 3;
+  const int64_t total = M * vpr;
+  const int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  // Groups are TPG adjacent lanes aligned to TPG; total is a multiple of TPG,
+  // so a group is either wholly in range or wholly past the end. Lanes past
+  // the end load the last vector so every shuffle partner stays defined.
+  const int64_t vv = v < total ? v : total - 1;
+  const int64_t row = vv / vpr, cv = vv - row * vpr;
+  float f[8];
+  load8<XT>(x, row * ld_x + cv * 8, f);
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
+  a = wave_max_xor(a, TPG);
+  const float sc = group_scale<UE>(a, eps, qmax);
+  if (v >= total) return;
+  const Divider<UE> div(sc);
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = div(f[i], qmin, qmax);
+  *reinterpret_cast<uint2*>(q + row * K + cv * 8) = encode8<FP8>(y);
+  if ((cv & (TPG - 1)) == 0) s[row * (vpr / TPG) + cv / TPG] = sc;
+}
+
+template <int XT, bool FP8, bool UE, bool VEC>
+__global__ __launch_bounds__(kThreads) void quant_group_block(
+    const void* __restrict__ x, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
+    float* __restrict__ s, int64_t g, float eps, float qmin, float qmax) {
+  __shared__ float red[kThreads / kWave];
+  const int64_t groups_per_row = K / g;
+  const int64_t row = blockIdx.x / groups_per_row;
+  const int64_t j = blockIdx.x - row * groups_per_row;
+  const int64_t xb = row * ld_x + j * g;
+  const int64_t qb = row * K + j * g;
+  float a = 0.0f;
+  if constexpr (VEC) {
+    for (int64_t i = (int64_t)threadIdx.x * 8; i < g; i += kThreads * 8) {
+      float f[8];
+      load8<XT>(x, xb + i, f);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) a = fmaxf(a, fabsf(f[t]));
+    }
+  } else {
+    for (int64_t i = threadIdx.x; i < g; i += kThreads) a = fmaxf(a, fabsf(load1<XT>(x, xb + i)));
+  }
+  a = block_max(a, red);
+  const float sc = group_scale<UE>(a, eps, qmax);
+  if (threadIdx.x == 0) s[blockIdx.x] = sc;
+  const Divider<UE> div(sc);
+  if constexpr (VEC) {
+    for (int64_t i = (int64_t)threadIdx.x * 8; i < g; i += kThreads * 8) {
+      float f[8], y[8];
+      load8<XT>(x, xb + i, f);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) y[t] = div(f[t], qmin, qmax);
+      *reinterpret_cast<uint2*>(q + qb + i) = encode8<FP8>(y);
+    }
+  } else {
+    for (int64_t i = threadIdx.x; i < g; i += kThreads)
+      q[qb + i] = encode1<FP8>(div(load1<XT>(x, xb + i), qmin, qmax));
+  }
+}
+
+template <int XT, bool VEC>
+__global__ __launch_bounds__(kThreads) void amax_partials(const void* __restrict__ x, int64_t M,
+                                                         int64_t K, int64_t ld_x,
+                                                         float* __restrict__ partial) {
+  __shared__ float red[kThreads / kWave];
+  float a = 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  if constexpr (VEC) {
+    const int64_t vpr = K >> 3, total = M * vpr;
+    for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < total; v += stride) {
+      const int64_t row = v / vpr, cv = v - row * vpr;
+      float f[8];
+      load8<XT>(x, row * ld_x + cv * 8, f);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) a = fmaxf(a, fabsf(f[t]));
+    }
+  } else {
+    const int64_t total = M * K;
+    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += stride) {
+      const int64_t row = e / K, c = e - row * K;
+      a = fmaxf(a, fabsf(load1<XT>(x, row * ld_x + c)));
+    }
+  }
+  a = block_max(a, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = a;
+}
+
+template <int XT, bool FP8, bool UE, bool VEC, bool STATIC>
+__global__ __launch_bounds__(kThreads) void quant_tensor(
+    const void* __restrict__ x, int64_t M, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
+    float* __restrict__ s, const float* __restrict__ partial, int nparts, float eps, float qmin,
+    float qmax) {
+  __shared__ float red[kThreads / kWave];
+  float sc;
+  if constexpr (STATIC) {
+    sc = s[0];
+  } else {
+    float a = 0.0f;
+    for (int i = threadIdx.x; i < nparts; i += kThreads) a = fmaxf(a, partial[i]);
+    a = block_max(a, red);
+    sc = group_scale<UE>(a, eps, qmax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) s[0] = sc;
+  }
+  const Divider<UE> div(sc);
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  if constexpr (VEC) {
+    const int64_t vpr = K >> 3, total = M * vpr;
+    for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < total; v += stride) {
+      const int64_t row = v / vpr, cv = v - row * vpr;
+      float f[8], y[8];
+      load8<XT>(x, row * ld_x + cv * 8, f);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) y[t] = div(f[t], qmin, qmax);
+      *reinterpret_cast<uint2*>(q + row * K + cv * 8) = encode8<FP8>(y);
+    }
+  } else {
+    const int64_t total = M * K;
+    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += stride) {
+      const int64_t row = e / K, c = e - row * K;
+      q[row * K + c] = encode1<FP8>(div(load1<XT>(x, row * ld_x + c), qmin, qmax));
+    }
+  }
+}
+
+// ---- host dispatch -------------------------------------------------------------
+template <int XT, bool FP8, bool UE>
+hipError_t dispatch(const QuantArgs& a, hipStream_t st) {
+  const int esz = XT == Q8_F32 ? 4 : 2;
+  const bool vec = (a.K % 8 == 0) && (a.ld_x % (esz == 2 ? 8 : 4) == 0) &&
+                   ((uintptr_t)a.x % 16 == 0) && ((uintptr_t)a.q % 8 == 0);
+  uint8_t* q = static_cast<uint8_t*>(a.q);
+  const dim3 blk(kThreads);
+  if (a.mode == Q8_SCALE_PER_GROUP) {
+    const int64_t g = a.group_size;
+    const bool pow2 = g >= 8 && g <= 512 && (g & (g - 1)) == 0;
+    if (vec && pow2) {
+      const int64_t total = a.M * (a.K / 8);
+      const dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
+      switch ((int)(g / 8)) {
+#define Q8_WAVE_CASE(T)                                                                     \
+  case T:                                                                                   \
+    hipLaunchKernelGGL((quant_group_wave<XT, FP8, UE, T>), grid, blk, 0, st, a.x, a.M, a.K, \
+                       a.ld_x, q, a.s, a.eps, a.qmin, a.qmax);                              \
+    break;
+        Q8_WAVE_CASE(1) Q8_WAVE_CASE(2) Q8_WAVE_CASE(4) Q8_WAVE_CASE(8) Q8_WAVE_CASE(16)
+        Q8_WAVE_CASE(32) Q8_WAVE_CASE(64)
+#undef Q8_WAVE_CASE
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    }
+    const int64_t ngroups = a.M * (a.K / g);
+    if (ngroups > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)ngroups);
+    if (vec && g % 8 == 0)
+      hipLaunchKernelGGL((quant_group_block<XT, FP8, UE, true>), grid, blk, 0, st, a.x, a.K,
+                         a.ld_x, q, a.s, g, a.eps, a.qmin, a.qmax);
+    else
+      hipLaunchKernelGGL((quant_group_block<XT, FP8, UE, false>), grid, blk, 0, st, a.x, a.K,
+                         a.ld_x, q, a.s, g, a.eps, a.qmin, a.qmax);
+    return hipGetLastError();
+  }
+  // per-tensor modes: grid-stride kernels
+  const int64_t work = vec ? a.M * (a.K / 8) : a.M * a.K;
+  int64_t blocks = (work + kThreads - 1) / kThreads;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid((unsigned)blocks);
+  float* partial = static_cast<float*>(a.workspace);
+  if (a.mode == Q8_SCALE_PER_TENSOR_DYNAMIC) {
+    const int np = (int)(blocks < kTensorPartials ? blocks : kTensorPartials);
+    if (vec) {
+      hipLaunchKernelGGL((amax_partials<XT, true>), dim3(np), blk, 0, st, a.x, a.M, a.K, a.ld_x,
+                         partial);
+      hipLaunchKernelGGL((quant_tensor<XT, FP8, UE, true, false>), grid, blk, 0, st, a.x, a.M,
+                         a.K, a.ld_x, q, a.s, partial, np, a.eps, a.qmin, a.qmax);
+    } else {
+      hipLaunchKernelGGL((amax_partials<XT, false>), dim3(np), blk, 0, st, a.x, a.M, a.K, a.ld_x,
+                         partial);
+      hipLaunchKernelGGL((quant_tensor<XT, FP8, UE, false, false>), grid, blk, 0, st, a.x, a.M,
+                         a.K, a.ld_x, q, a.s, partial, np, a.eps, a.qmin, a.qmax);
+    }
+  } else if (vec) {
+    hipLaunchKernelGGL((quant_tensor<XT, FP8, false, true, true>), grid, blk, 0, st, a.x, a.M,
+                       a.K, a.ld_x, q, a.s, nullptr, 0, a.eps, a.qmin, a.qmax);
+  } else {
+    hipLaunchKernelGGL((quant_tensor<XT, FP8, false, false, true>), grid, blk, 0, st, a.x, a.M,
+                       a.K, a.ld_x, q, a.s, nullptr, 0, a.eps, a.qmin, a.qmax);
+  }
+  return hipGetLastError();
+}
+
+template <int XT>
+hipError_t dispatch_q(const QuantArgs& a, hipStream_t st) {
+  const bool ue = a.ue8m0 != 0 && a.mode != Q8_SCALE_STATIC;
+  if (a.q_dtype == Q8_E4M3FN)
+    return ue ? dispatch<XT, true, true>(a, st) : dispatch<XT, true, false>(a, st);
+  return ue ? dispatch<XT, false, true>(a, st) : dispatch<XT, false, false>(a, st);
+}
+
+}  // namespace
+
+size_t quant_partials_count(int64_t, int64_t) { return kTensorPartials; }
+
+hipError_t launch_quant(const QuantArgs& a, hipStream_t st) {
+  switch (a.x_dtype) {
+    case Q8_F32: return dispatch_q<Q8_F32>(a, st);
+    case Q8_BF16: return dispatch_q<Q8_BF16>(a, st);
+    case Q8_F16: return dispatch_q<Q8_F16>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace q8

@@ -1,0 +1,40 @@
+// Shared pieces of the LDS-tiled MFMA GEMM kernels (FP8 block-scaled and INT8).
+//
+// LDS tile layout: a [rows x 128 B] K-slab per stage, one 128-byte line per
+// row, split into eight 16-byte chunks. Chunk c of row r is stored at chunk
+// position c ^ (r & 7), so eight lanes reading the same logical chunk of eight
+// consecutive rows hit eight different 16-byte bank groups (no conflicts for
+// ds_read_b128), and the row-contiguous global loads stay fully coalesced.
+#pragma once
+
+#include "q8_device.h"
+
+namespace q8 {
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+// Blocks of a launch are spread round-robin over the 8 XCDs (each with its
+// own L2). Renumber them so that consecutive logical tiles land on the same
+// XCD: block b runs on XCD b % 8, and logical ids are handed out to XCDs in
+// contiguous runs. Bijective on [0, total).
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t total) {
+  constexpr int kXcd = 8;
+  const int64_t base = total / kXcd, rem = total % kXcd;
+  const int64_t x = b % kXcd, i = b / kXcd;
+  return x < rem ? x * (base + 1) + i : rem * (base + 1) + (x - rem) * base + i;
+}
+
+// Logical tile id -> (tm, tn), walking GM tile-rows at a time so that the
+// tiles resident together share A rows and W rows in L2.
+__device__ __forceinline__ void grouped_order(int64_t t, int64_t tiles_m, int64_t tiles_n, int gm,
+                                              int64_t& tm, int64_t& tn) {
+  const int64_t per_group = (int64_t)gm * tiles_n;
+  const int64_t group = t / per_group;
+  const int64_t first_m = group * gm;
+  const int64_t rows = tiles_m - first_m < gm ? tiles_m - first_m : gm;
+  const int64_t r = t - group * per_group;
+  tm = first_m + r % rows;
+  tn = r / rows;
+}
+
+}  // namespace q8

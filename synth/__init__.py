@@ -69,26 +69,41 @@ def bias(N: int, dtype: str = "bf16", sigma: float = 1.0, seed: int = 0) -> torc
     return t.to(torch.bfloat16 if dtype == "bf16" else torch.float16)
 
 
+def _quantize_block_tile_rows(w: np.ndarray, bn: int, bk: int):
+    """One [N, K] float32 weight -> (e4m3fn codes [N, K] uint8, scales [nb, kb])."""
+    N, K = w.shape
+    nb, kb = -(-N // bn), -(-K // bk)
+    pad = np.zeros((nb * bn, kb * bk), dtype=np.float32)
+    pad[:N, :K] = np.abs(w)
+    amax = pad.reshape(nb, bn, kb, bk).max(axis=(1, 3))
+    ws = (np.maximum(amax, np.float32(1e-12)) / np.float32(E4M3_MAX)).astype(np.float32)
+    full = np.repeat(np.repeat(ws, bn, axis=0), bk, axis=1)[:N, :K]
+    ratio = np.clip(w / full, -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    codes = torch.from_numpy(ratio).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, ws
+
+
 def fp8_block_weights(N: int, K: int, bn: int, bk: int, sigma: float = 0.02,
                       seed: int = 0, tag: int = TAG_W, experts: int | None = None):
     """Checkpoint-style block-FP8 weights.
 
     Returns ``(Wq, Ws)``: ``Wq`` is ``[N, K]`` (or ``[E, N, K]``) uint8 holding
     e4m3fn codes, ``Ws`` is ``[ceil(N/bn), ceil(K/bk)]`` (or ``[E, ...]``)
-    float32, one scale per weight tile.
+    float32, one scale per weight tile. Experts are drawn one after another
+    from the same stream, expert 0 first.
     """
-    shape = (N, K) if experts is None else (experts, N, K)
-    w = normal_f32(shape, sigma, seed, tag)
-    lead = shape[:-2]
+    g = rng(seed, tag)
+    E = 1 if experts is None else experts
     nb, kb = -(-N // bn), -(-K // bk)
-    pad = np.zeros(lead + (nb * bn, kb * bk), dtype=np.float32)
-    pad[..., :N, :K] = np.abs(w)
-    amax = pad.reshape(lead + (nb, bn, kb, bk)).max(axis=(-3, -1))
-    ws = (np.maximum(amax, np.float32(1e-12)) / np.float32(E4M3_MAX)).astype(np.float32)
-    full = np.repeat(np.repeat(ws, bn, axis=-2), bk, axis=-1)[..., :N, :K]
-    ratio = np.clip(w / full, -E4M3_MAX, E4M3_MAX).astype(np.float32)
-    wq = torch.from_numpy(ratio).to(torch.float8_e4m3fn).view(torch.uint8)
-    return wq.contiguous(), torch.from_numpy(np.ascontiguousarray(ws))
+    wq = torch.empty((E, N, K), dtype=torch.uint8)
+    ws = np.empty((E, nb, kb), dtype=np.float32)
+    for e in range(E):
+        w = (g.standard_normal(size=(N, K), dtype=np.float32) * np.float32(sigma)).astype(np.float32)
+        wq[e], ws[e] = _quantize_block_tile_rows(w, bn, bk)
+    ws_t = torch.from_numpy(ws)
+    if experts is None:
+        return wq[0].contiguous(), ws_t[0].contiguous()
+    return wq, ws_t
 
 
 def int8_weights(N: int, K: int, per_channel: bool = True, sigma: float = 0.02,

@@ -1,0 +1,125 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects invalid
+calls with the documented status codes before touching the device.
+
+Runs without a GPU: every call here fails host-side validation (or is a
+documented no-op), so no HIP API is reached.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "int8_quantized_gemm_amd", "libq8gemm.so")
+HEADER = os.path.join(ROOT, "include", "q8gemm.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libq8gemm.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s+\**([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def q8():
+    import int8_quantized_gemm_amd as m
+    return m
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for n in ("quant_8bit", "blockwise_scaled_mm", "scaled_mm_int8", "moe_mm_data",
+              "grouped_blockwise_scaled_mm", "shuffle_rows", "q8gemm_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(q8):
+    lib = ctypes.CDLL(LIB)
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(q8.EXPORTS) == names
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import subprocess
+    import sys
+    code = ("import sys, os; sys.path.insert(0, %r); import builtins;"
+            "real = os.path.exists;"
+            "os.path.exists = lambda p: False if p.endswith('libq8gemm.so') else real(p);"
+            "import int8_quantized_gemm_amd") % ROOT
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
+    assert r.returncode != 0 and "libq8gemm.so" in r.stderr and "ImportError" in r.stderr
+
+
+def test_quant_validation(q8):
+    L = q8._lib
+    f, p = ctypes.c_float, None
+    # bad input dtype
+    assert q8._quant(p, 7, 4, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 0, p, p, 0, p) == q8.Q8_EINVAL
+    assert "x_dtype" in q8.last_error()
+    # group does not divide K
+    assert q8._quant(p, q8.Q8_BF16, 4, 100, 100, p, q8.Q8_E4M3FN, p, 32, 0, 1e-10, -448, 448, 0, 0, p, p, 0, p) == q8.Q8_ESHAPE
+    # FP8 clip range beyond 448
+    assert q8._quant(p, q8.Q8_BF16, 4, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -480, 480, 0, 0, p, p, 0, p) == q8.Q8_EINVAL
+    # fused SiLU-and-mul, masked_m not implemented
+    assert q8._quant(p, q8.Q8_BF16, 4, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 1, p, p, 0, p) == q8.Q8_EUNSUPPORTED
+    assert q8._quant(p, q8.Q8_BF16, 4, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 0, 8, p, 0, p) == q8.Q8_EUNSUPPORTED
+    # ld_x < K
+    assert q8._quant(p, q8.Q8_BF16, 4, 128, 64, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 0, p, p, 0, p) == q8.Q8_ESHAPE
+    # null pointers with real work
+    assert q8._quant(p, q8.Q8_BF16, 4, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 0, p, p, 0, p) == q8.Q8_EINVAL
+    # per-tensor dynamic needs workspace
+    need = q8._quant_ws(4, 128, q8.SCALE_PER_TENSOR_DYNAMIC)
+    assert need > 0 and q8._quant_ws(4, 128, q8.SCALE_PER_GROUP) == 0
+    assert q8._quant(8, q8.Q8_BF16, 4, 128, 128, 8, q8.Q8_E4M3FN, 8, 128, 1, 1e-10, -448, 448, 0, 0, p, p, 0, p) == q8.Q8_EWORKSPACE
+    # UE8M0 with a static scale is rejected
+    assert q8._quant(8, q8.Q8_BF16, 4, 128, 128, 8, q8.Q8_E4M3FN, 8, 128, 2, 1e-10, -448, 448, 1, 0, p, p, 0, p) == q8.Q8_EINVAL
+    # empty input is a no-op (no pointer needed)
+    assert q8._quant(p, q8.Q8_BF16, 0, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 0, p, p, 0, p) == q8.Q8_OK
+    assert q8.last_error() == ""
+
+
+def test_blockwise_validation(q8):
+    p = None
+    args = lambda M, N, K, bn, bk, out=q8.Q8_BF16: (p, p, p, p, p, p, out, M, N, K, bn, bk, p, 0, p)
+    assert q8._bmm(*args(4, 256, 500, 128, 128)) == q8.Q8_ESHAPE          # ragged K
+    assert "multiple of bk" in q8.last_error()
+    assert q8._bmm(*args(4, 256, 512, 128, 64)) == q8.Q8_EUNSUPPORTED     # bk not in {32, 128}
+    assert q8._bmm(*args(4, 256, 512, 24, 128)) == q8.Q8_EUNSUPPORTED     # bn not a multiple of 16
+    assert q8._bmm(*args(4, 256, 512, 128, 128, q8.Q8_F32)) == q8.Q8_EINVAL
+    assert q8._bmm(*args(4, 256, 512, 128, 128)) == q8.Q8_EINVAL          # null pointers
+    assert q8._bmm(*args(0, 256, 512, 128, 128)) == q8.Q8_OK              # M = 0
+    assert q8._bmm(*args(-1, 256, 512, 128, 128)) == q8.Q8_ESHAPE
+
+
+def test_int8_validation(q8):
+    p = None
+    assert q8._imm(p, p, 1, p, p, 1, p, p, q8.Q8_BF16, 4, 100, 128, p) == q8.Q8_ESHAPE   # N % 16
+    assert q8._imm(p, p, 1, p, p, 1, p, p, q8.Q8_BF16, 4, 128, 120, p) == q8.Q8_ESHAPE   # K % 16
+    assert q8._imm(p, 8, 3, p, 8, 1, p, p, q8.Q8_BF16, 4, 128, 128, p) == q8.Q8_EUNSUPPORTED
+    assert "scales_a" in q8.last_error()
+    assert q8._imm(p, 8, 4, p, 8, 7, p, p, q8.Q8_BF16, 4, 128, 128, p) == q8.Q8_EUNSUPPORTED
+    assert q8._imm(p, 8, 1, p, p, 1, p, p, q8.Q8_I32, 4, 128, 128, p) == q8.Q8_EINVAL    # scales with I32
+    assert q8._imm(p, 8, 1, p, 8, 1, p, p, q8.Q8_F32, 4, 128, 128, p) == q8.Q8_EINVAL
+    assert q8._imm(p, 8, 1, p, 8, 1, p, p, q8.Q8_BF16, 0, 128, 128, p) == q8.Q8_OK
+
+
+def test_moe_and_grouped_validation(q8):
+    p = None
+    assert q8._moe(p, 16, 8, 0, 64, 64, p, p, p, p, p, p, 0, p) == q8.Q8_EUNSUPPORTED   # E = 0
+    assert q8._moe(p, 16, 8, 2000, 64, 64, p, p, p, p, p, p, 0, p) == q8.Q8_EUNSUPPORTED
+    assert q8._moe(p, 16, 0, 8, 64, 64, p, p, p, p, p, p, 0, p) == q8.Q8_ESHAPE
+    assert q8._moe(8, 16, 8, 8, 64, 64, 8, 8, 8, 8, 8, p, 0, p) == q8.Q8_EWORKSPACE
+    assert q8._moe_ws(4096, 8, 64) == (4096 * 8 // 256) * 64 * 4
+    g = lambda tm, K, cmap=p, ws=p, wsb=0: (8, 8, 8, 8, 8, q8.Q8_BF16, 8, 8, p, cmap, 4, tm, 256, K, 128, 128, ws, wsb, p)
+    assert q8._gmm(*g(64, 500)) == q8.Q8_ESHAPE
+    assert q8._gmm(*g(64, 512, cmap=8)) == q8.Q8_EWORKSPACE
+    assert q8._gmm(*g(0, 512)) == q8.Q8_OK
+    assert q8._shuf(p, 16, p, 4, p, p) == q8.Q8_EINVAL
+    assert q8._shuf(p, 16, p, 0, p, p) == q8.Q8_OK

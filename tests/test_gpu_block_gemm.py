@@ -1,0 +1,134 @@
+"""GPU parity: activation quant + block-scaled FP8 GEMM against the oracle.
+
+Each side runs the whole hot path from the same seeded bf16/fp32 activations
+and checkpoint-style weights: the GPU quantizes with its kernel and multiplies
+with its kernel; the oracle quantizes and multiplies in numpy (exact fp8
+decode, float64 accumulation). Quantized bytes must match exactly; GEMM
+outputs must satisfy |D - D_ref| <= 1e-2 |D_ref| + 1e-3 rms(D_ref).
+Full-size prefill shapes are checked on sampled rows (the oracle computes
+those rows one by one; the GPU still computes the whole output).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import gemm as og
+from oracle import quant as oq
+from tests.gpu_util import DEV, assert_gemm_close, codes, q8, sync
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-10
+
+
+def gpu_path(x_dev, Wq, Ws, g, ue, bn, bk, bias=None, out_dtype=torch.bfloat16):
+    m = q8()
+    M, K = x_dev.shape
+    aq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=DEV)
+    As = torch.empty((M, K // g), dtype=torch.float32, device=DEV)
+    m.quant_8bit(x_dev, aq, As, g, EPS, -448.0, 448.0, ue)
+    d = m.blockwise_scaled_mm(aq, Wq.to(DEV), As, Ws.to(DEV), out_dtype,
+                              None if bias is None else bias.to(DEV), block=(bn, bk))
+    sync()
+    return aq, As, d
+
+
+def oracle_path(x_cpu, Wq, Ws, g, ue, bn, bk, bias=None, rows=None):
+    x = x_cpu.float().numpy()
+    if rows is not None:
+        x = x[rows]
+    aq, As = oq.per_token_group(x, g, EPS, -448.0, 448.0, ue, "e4m3")
+    b = None if bias is None else bias.float().numpy()
+    return aq, As, og.blockwise_scaled_mm(aq, As, Wq.numpy(), Ws.numpy(), bn, bk, bias=b)
+
+
+def run_case(M, N, K, bn, bk, *, ue=False, x_dtype="bf16", outliers=0.0, bias=False,
+             rows=None, seed=0, out_dtype=torch.bfloat16):
+    x = synth.activations(M, K, x_dtype, outlier_frac=outliers, seed=seed)
+    Wq, Ws = synth.fp8_block_weights(N, K, bn, bk, seed=seed)
+    b = synth.bias(N, "bf16" if out_dtype == torch.bfloat16 else "f16", seed=seed) if bias else None
+    aq_g, as_g, d = gpu_path(x.to(DEV), Wq, Ws, bk, ue, bn, bk, b, out_dtype)
+    aq_o, as_o, ref = oracle_path(x, Wq, Ws, bk, ue, bn, bk, b, rows)
+    sel = slice(None) if rows is None else rows
+    assert np.array_equal(codes(aq_g)[sel], aq_o)
+    assert np.array_equal(as_g.cpu().numpy()[sel], as_o)
+    assert_gemm_close(d[sel] if rows is None else d[torch.as_tensor(rows, device=DEV)], ref,
+                      f"M={M} N={N} K={K} bn={bn} bk={bk}")
+    return d
+
+
+def sample_rows(M, n=48, seed=0):
+    r = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, M - 1], r.choice(M, size=n, replace=False)]))
+
+
+def test_tiny_fp32_block128():
+    run_case(4, 256, 512, 128, 128, x_dtype="f32")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 64])
+def test_decode_block32_ue8m0(M):
+    run_case(M, 4096, 7168, 32, 32, ue=True, outliers=0.01)
+
+
+@pytest.mark.parametrize("N", [7168, 18432])
+@pytest.mark.parametrize("bias", [False, True])
+def test_prefill_full_size_sampled_rows(N, bias):
+    run_case(4096, N, 7168, 128, 128, bias=bias, rows=sample_rows(4096))
+
+
+@pytest.mark.parametrize("M,N,K", [(65, 256, 256), (300, 520, 1024), (513, 1000, 512),
+                                   (257, 16, 384), (96, 4096, 7168)])
+@pytest.mark.parametrize("bk", [128, 32])
+def test_tile_shapes_ragged(M, N, K, bk):
+    run_case(M, N, K, bk, bk, ue=(bk == 32), bias=True, seed=M + N)
+
+
+@pytest.mark.parametrize("bn", [48, 64, 256])
+def test_weight_block_rows_differ_from_bk(bn):
+    run_case(200, 600, 512, bn, 128, seed=3)
+    run_case(10, 600, 512, bn, 128, seed=4)
+
+
+@pytest.mark.parametrize("M", [3, 100])
+def test_k_not_multiple_of_128(M):
+    run_case(M, 200, 96, 32, 32, seed=5)
+
+
+def test_f16_output_and_bias():
+    run_case(130, 384, 1024, 128, 128, bias=True, out_dtype=torch.float16, seed=6)
+    run_case(7, 384, 1024, 128, 128, bias=True, out_dtype=torch.float16, seed=7)
+
+
+def test_one_hot_weights_gather_exactly():
+    """W row n holds a single 1.0 at column pi(n) with unit weight scales, so
+    D[m, n] = As[m, pi(n)/bk] * A[m, pi(n)]: one float32 product, then bf16.
+    Equality catches transposed operands and scale mis-indexing."""
+    m = q8()
+    M, N, K, bk = 130, 256, 1024, 128
+    r = np.random.default_rng(0)
+    pi = r.permutation(K)[:N]
+    Wq = torch.zeros((N, K), dtype=torch.uint8)
+    Wq[torch.arange(N), torch.from_numpy(pi)] = 0x38
+    Ws = torch.ones(((N + bk - 1) // bk, K // bk), dtype=torch.float32)
+    x = synth.activations(M, K, "bf16", seed=1)
+    for Mx in (M, 9):
+        aq_g, as_g, d = gpu_path(x[:Mx].to(DEV), Wq, Ws, bk, False, bk, bk)
+        aq_o, as_o = oq.per_token_group(x[:Mx].float().numpy(), bk, EPS, -448.0, 448.0, False, "e4m3")
+        from oracle import e4m3
+        expect = as_o[:, pi // bk].astype(np.float32) * e4m3.decode(aq_o[:, pi]).astype(np.float32)
+        expect_bf16 = torch.from_numpy(expect).to(torch.bfloat16).double().numpy()
+        assert np.array_equal(d.cpu().double().numpy(), expect_bf16)
+
+
+def test_run_twice_identical_and_zero_m():
+    m = q8()
+    x = synth.activations(300, 1024, "bf16", seed=2).to(DEV)
+    Wq, Ws = synth.fp8_block_weights(512, 1024, 128, 128, seed=2)
+    d1 = gpu_path(x, Wq, Ws, 128, False, 128, 128)[2]
+    d2 = gpu_path(x, Wq, Ws, 128, False, 128, 128)[2]
+    assert torch.equal(d1, d2)
+    e = m.blockwise_scaled_mm(torch.empty((0, 1024), dtype=torch.float8_e4m3fn, device=DEV),
+                              Wq.to(DEV), torch.empty((0, 8), device=DEV), Ws.to(DEV))
+    assert e.shape == (0, 512)
