@@ -43,6 +43,7 @@ struct TileParams {
   int bn;
   int nbw;        // ceil(N / bn): weight-scale rows (per expert)
   int out_bf16;
+  int d_vec4;     // N % 4 == 0 and D (and bias) 8-byte aligned: 8-byte stores
   int64_t tiles_m, tiles_n;
   // expert-grouped variant
   const int32_t* offsets;  // [E+1] slot ranges per expert
@@ -93,23 +94,89 @@ __device__ __forceinline__ uint16_t to_out_bits(float v, bool bf16) {
 // ------------------------------------------------------------------------------
 // LDS-tiled kernel
 // ------------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int KS, bool GROUPED>
-__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile(TileParams p) {
-  constexpr int NT = WM * WN * 64;
+#define Q8_AS1 __attribute__((address_space(1)))
+#define Q8_AS3 __attribute__((address_space(3)))
+
+// Direct global -> LDS loads (no staging registers): lane l of the wave writes
+// its 16 (or 4) bytes at lds + 16*l (4*l); lds must be wave-uniform.
+__device__ __forceinline__ void g2l16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((Q8_AS1 void*)g, (Q8_AS3 void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void g2l4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((Q8_AS1 void*)g, (Q8_AS3 void*)lds, 4, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ i32x8 lds_frag32(const uint8_t* base, int row, int g) {
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(base + swz(row, 2 * g));
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(base + swz(row, 2 * g + 1));
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ long lds_frag8(const uint8_t* base, int row, int s, int g) {
+  return *reinterpret_cast<const long*>(base + swz(row, 2 * s + (g >> 1)) + (g & 1) * 8);
+}
+
+// Store four consecutive outputs D[row, n .. n+3] (+ bias) as 16-bit values.
+__device__ __forceinline__ void store4(const TileParams& p, int64_t row, int64_t n, f32x4 v,
+                                       bool bf16, bool vec) {
+  uint16_t* D = static_cast<uint16_t*>(p.D);
+  const int64_t N = p.N;
+  if (vec && n + 3 < N) {
+    if (p.bias) {
+      const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.bias) + n);
+      const uint32_t bw[4] = {b.x & 0xFFFFu, b.x >> 16, b.y & 0xFFFFu, b.y >> 16};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] += bf16 ? bf16_bits_to_f32(bw[r]) : f16_bits_to_f32(bw[r]);
+    }
+    uint2 o;
+    o.x = (uint32_t)to_out_bits(v[0], bf16) | ((uint32_t)to_out_bits(v[1], bf16) << 16);
+    o.y = (uint32_t)to_out_bits(v[2], bf16) | ((uint32_t)to_out_bits(v[3], bf16) << 16);
+    *reinterpret_cast<uint2*>(D + row * N + n) = o;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (n + r >= N) break;
+      const float bv = p.bias ? load_out_f32(p.bias, n + r, bf16) : 0.0f;
+      D[row * N + n + r] = to_out_bits(v[r] + bv, bf16);
+    }
+  }
+}
+
+// BM x BN output tile per workgroup of WM x WN waves; each wave owns a
+// (BM/WM) x (BN/WN) sub-tile made of 16 x 16 MFMA blocks. MFMA operand 0 is
+// the weight fragment and operand 1 the activation fragment, so a lane's
+// four accumulators are four consecutive output columns of one row: one
+// activation-scale value per row block, and 8-byte output stores.
+// WSU: every 16-column block of a wave lies in the same weight-scale block.
+template <int BM, int BN, int WM, int WN, int KS, bool GROUPED, bool WSU>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
+  constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
   constexpr int KSUB = 128 / KS;
-  constexpr int A_CH = BM * 8 / NT, B_CH = BN * 8 / NT;
-  constexpr int S_TOT = BM * KSUB, S_PER = (S_TOT + NT - 1) / NT;
-  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/thread mismatch");
-  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+  constexpr int A_SLOTS = BM / 8, B_SLOTS = BN / 8;  // 1 KB (8 rows) per wave load
+  constexpr int A_PER = (A_SLOTS + NW - 1) / NW, B_PER = (B_SLOTS + NW - 1) / NW;
+  constexpr int S_SLOTS = BM * KSUB / 64;            // 64 scales per wave load
+  constexpr int S_PER = (S_SLOTS + NW - 1) / NW;
+  static_assert(TM % 16 == 0 && TN % 16 == 0 && FM % 4 == 0, "wave tile");
+  static_assert(BM % 8 == 0 && BN % 8 == 0 && (BM * KSUB) % 64 == 0, "tile");
 
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * 128];
-  __shared__ __attribute__((aligned(16))) float sS[2][KSUB][BM];
+  // Two stages in separate arrays: the compiler can then tell that the LDS
+  // reads of one stage never alias the in-flight global->LDS loads of the
+  // other and does not wait for those loads before computing.
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * 128];
+  // activation scales of a stage, [KSUB][WM][16][FM]: a lane's FM row-block
+  // scales are contiguous
+  __shared__ __attribute__((aligned(16))) float sS0[KSUB * BM];
+  __shared__ __attribute__((aligned(16))) float sS1[KSUB * BM];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid / WN, wn = wid % WN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w / WN, wn = w % WN;
   const int g = lane >> 4, r16 = lane & 15;
   const int64_t N = p.N, K = p.K;
   const int KB = p.KB;
@@ -147,72 +214,56 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile(TileParams p) {
   const float* Wsb = p.Ws + (GROUPED ? (int64_t)e * p.nbw * KB : 0);
 
   auto a_row = [&](int64_t slot) -> int64_t {
-    if constexpr (GROUPED) return p.a_map ? (int64_t)p.a_map[slot] : slot;
-    else return slot;
+    const int64_t s = slot < m_hi ? slot : m_hi - 1;  // rows past the end re-read the last row
+    if constexpr (GROUPED) return p.a_map ? (int64_t)p.a_map[s] : s;
+    else return s;
   };
 
-  // ---- per-thread staging sources (rows past the end re-read the last valid
-  // row; their results are never stored)
-  const uint8_t* a_src[A_CH];
-  const uint8_t* b_src[B_CH];
+  // ---- per-lane global sources of this wave's LDS loads. Wave load q of a
+  // stage fills rows 8q..8q+7; lane l writes physical chunk l%8 of row
+  // 8q + l/8, which holds logical chunk (l%8) ^ (row%8).
+  // 32-bit byte offsets from uniform bases (the host guarantees every operand
+  // is below 4 GiB), so each load is a scalar base + one VGPR
+  uint32_t a_off[A_PER], b_off[B_PER], s_off[S_PER];
 #pragma unroll
-  for (int c = 0; c < A_CH; ++c) {
-    const int idx = tid + c * NT, r = idx >> 3, ch = idx & 7;
-    const int64_t slot = m_lo + r < m_hi ? m_lo + r : m_hi - 1;
-    a_src[c] = p.A + a_row(slot) * K + ch * 16;
+  for (int c = 0; c < A_PER; ++c) {
+    const int q = w + c * NW < A_SLOTS ? w + c * NW : 0;
+    const int row = 8 * q + (lane >> 3), lch = (lane & 7) ^ (row & 7);
+    a_off[c] = (uint32_t)(a_row(m_lo + row) * K + lch * 16);
   }
 #pragma unroll
-  for (int c = 0; c < B_CH; ++c) {
-    const int idx = tid + c * NT, r = idx >> 3, ch = idx & 7;
-    const int64_t n = n0 + r < N ? n0 + r : N - 1;
-    b_src[c] = Wb + n * K + ch * 16;
+  for (int c = 0; c < B_PER; ++c) {
+    const int q = w + c * NW < B_SLOTS ? w + c * NW : 0;
+    const int row = 8 * q + (lane >> 3), lch = (lane & 7) ^ (row & 7);
+    const int64_t n = n0 + row < N ? n0 + row : N - 1;
+    b_off[c] = (uint32_t)(n * K + lch * 16);
   }
-  const float* s_src[S_PER];
-  int s_dst[S_PER];
 #pragma unroll
   for (int c = 0; c < S_PER; ++c) {
-    const int idx = tid + c * NT;
-    const int r = idx % BM, s = idx / BM;
-    const int64_t slot = m_lo + r < m_hi ? m_lo + r : m_hi - 1;
-    s_src[c] = p.As + a_row(slot) * KB + s;
-    s_dst[c] = idx < S_TOT ? idx : -1;  // flat [KSUB][BM] index within a stage
+    const int q = w + c * NW < S_SLOTS ? w + c * NW : 0;
+    const int f = 64 * q + lane;
+    const int s = f / BM, rem = f % BM;
+    const int wmm = rem / TM, r2 = rem % TM;
+    const int row = wmm * TM + (r2 % FM) * 16 + r2 / FM;
+    s_off[c] = (uint32_t)((a_row(m_lo + row) * KB + s) * 4);
   }
-
-  uint4 ra[A_CH], rb[B_CH];
-  float rs[S_PER];
-  auto gload = [&](int kt) {
+  const uint8_t* As_bytes = reinterpret_cast<const uint8_t*>(p.As);
+  auto issue = [&](int kt, uint8_t* __restrict__ la, uint8_t* __restrict__ lb, float* __restrict__ ls) {
+    const uint8_t* ab = p.A + kt * 128;
+    const uint8_t* bb = Wb + kt * 128;
+    const uint8_t* sb = As_bytes + kt * KSUB * 4;
 #pragma unroll
-    for (int c = 0; c < A_CH; ++c) ra[c] = *reinterpret_cast<const uint4*>(a_src[c] + kt * 128);
+    for (int c = 0; c < A_PER; ++c)
+      if (A_SLOTS % NW == 0 || w + c * NW < A_SLOTS) g2l16(ab + a_off[c], la + (w + c * NW) * 1024);
 #pragma unroll
-    for (int c = 0; c < B_CH; ++c) rb[c] = *reinterpret_cast<const uint4*>(b_src[c] + kt * 128);
-#pragma unroll
-    for (int c = 0; c < S_PER; ++c)
-      if (s_dst[c] >= 0) rs[c] = s_src[c][kt * KSUB];
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < A_CH; ++c) {
-      const int idx = tid + c * NT;
-      *reinterpret_cast<uint4*>(&sA[buf][swz(idx >> 3, idx & 7)]) = ra[c];
-    }
-#pragma unroll
-    for (int c = 0; c < B_CH; ++c) {
-      const int idx = tid + c * NT;
-      *reinterpret_cast<uint4*>(&sB[buf][swz(idx >> 3, idx & 7)]) = rb[c];
-    }
+    for (int c = 0; c < B_PER; ++c)
+      if (B_SLOTS % NW == 0 || w + c * NW < B_SLOTS) g2l16(bb + b_off[c], lb + (w + c * NW) * 1024);
 #pragma unroll
     for (int c = 0; c < S_PER; ++c)
-      if (s_dst[c] >= 0) (&sS[buf][0][0])[s_dst[c]] = rs[c];
+      if (S_SLOTS % NW == 0 || w + c * NW < S_SLOTS) g2l4(sb + s_off[c], ls + (w + c * NW) * 64);
   };
 
-  f32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // weight-scale row for each 16-column block of this wave (clamped for
-  // ragged N; those columns are never stored)
+  // weight-scale rows of this wave's 16-column blocks (clamped for ragged N)
   const float* ws_row[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
@@ -221,89 +272,112 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_tile(TileParams p) {
     ws_row[j] = Wsb + nb * KB;
   }
 
-  const int KT = (int)(K / 128);
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const uint8_t* la = sA[buf];
-    const uint8_t* lb = sB[buf];
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Weight scales of stage kt are loaded (into registers) before the loads of
+  // stage kt+1 are issued, so using them never waits on those loads (vector
+  // memory completes in order).
+  float wsv[KSUB][FN];
+  auto load_ws = [&](int kt) {
+#pragma unroll
+    for (int s = 0; s < KSUB; ++s)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) wsv[s][j] = (WSU && j > 0) ? 0.0f : ws_row[j][kt * KSUB + s];
+  };
+  auto compute = [&](const uint8_t* la, const uint8_t* lb, const float* ls, const float (&wv)[KSUB][FN]) {
 #pragma unroll
     for (int s = 0; s < KSUB; ++s) {
-      const int kb = kt * KSUB + s;
-      float wsc[FN];
+      float ws[FN];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) wsc[j] = ws_row[j][kb];
+      for (int j = 0; j < FN; ++j) ws[j] = WSU ? wv[s][0] : wv[s][j];
+      float sa[FM];
+#pragma unroll
+      for (int i4 = 0; i4 < FM / 4; ++i4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ls + s * BM + wm * TM + r16 * FM + 4 * i4);
+        sa[4 * i4] = v[0]; sa[4 * i4 + 1] = v[1]; sa[4 * i4 + 2] = v[2]; sa[4 * i4 + 3] = v[3];
+      }
       if constexpr (KS == 128) {
-        i32x8 bf[FN];
+        i32x8 bw[FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int row = wn * TN + j * 16 + r16;
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(lb + swz(row, 2 * g));
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(lb + swz(row, 2 * g + 1));
-          bf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
+        for (int j = 0; j < FN; ++j) bw[j] = lds_frag32(lb, wn * TN + j * 16 + r16, g);
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          const int row = wm * TM + i * 16 + r16;
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(la + swz(row, 2 * g));
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(la + swz(row, 2 * g + 1));
-          const i32x8 af = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const f32x4 sa = *reinterpret_cast<const f32x4*>(&sS[buf][s][wm * TM + i * 16 + 4 * g]);
+          const i32x8 av = lds_frag32(la, wm * TM + i * 16 + r16, g);
+          f32x4 pr[FN];
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const f32x4 pr = mfma_fp8_k128(af, bf[j]);
-            acc[i][j] = fma4(pr, sa * wsc[j], acc[i][j]);
-          }
+          for (int j = 0; j < FN; ++j) pr[j] = mfma_fp8_k128(bw[j], av);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = fma4s(pr[j], sa[i] * ws[j], acc[i][j]);
         }
       } else {
-        long bf[FN];
+        long bw[FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int row = wn * TN + j * 16 + r16;
-          bf[j] = *reinterpret_cast<const long*>(lb + swz(row, 2 * s + (g >> 1)) + (g & 1) * 8);
-        }
+        for (int j = 0; j < FN; ++j) bw[j] = lds_frag8(lb, wn * TN + j * 16 + r16, s, g);
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          const int row = wm * TM + i * 16 + r16;
-          const long af = *reinterpret_cast<const long*>(la + swz(row, 2 * s + (g >> 1)) + (g & 1) * 8);
-          const f32x4 sa = *reinterpret_cast<const f32x4*>(&sS[buf][s][wm * TM + i * 16 + 4 * g]);
+          const long av = lds_frag8(la, wm * TM + i * 16 + r16, s, g);
+          f32x4 pr[FN];
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const f32x4 pr = mfma_fp8_k32(af, bf[j]);
-            acc[i][j] = fma4(pr, sa * wsc[j], acc[i][j]);
-          }
+          for (int j = 0; j < FN; ++j) pr[j] = mfma_fp8_k32(bw[j], av);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = fma4s(pr[j], sa[i] * ws[j], acc[i][j]);
         }
       }
     }
-    if (kt + 1 < KT) lstore(buf ^ 1);
+  };
+
+  // Stage kt lives in buffer kt % 2; one barrier per stage: after it, stage kt
+  // has landed for every wave and stage kt-1 (the other buffer) is no longer
+  // read, so it is refilled while stage kt is computed. The refill and the
+  // compute go through restrict-qualified pointers of one inlined step, which
+  // tells the compiler that the LDS reads never alias the in-flight
+  // global->LDS writes (otherwise it waits for those loads before every read).
+  auto step = [&](int kt, bool refill, uint8_t* __restrict__ na, uint8_t* __restrict__ nb,
+                  float* __restrict__ ns, const uint8_t* __restrict__ la,
+                  const uint8_t* __restrict__ lb, const float* __restrict__ ls) {
+    float wcur[KSUB][FN];
+#pragma unroll
+    for (int s = 0; s < KSUB; ++s)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) wcur[s][j] = wsv[s][j];
+    if (refill) {
+      load_ws(kt + 1);
+      issue(kt + 1, na, nb, ns);
+    }
+    compute(la, lb, ls, wcur);
+  };
+  const int KT = (int)(K / 128);
+  load_ws(0);
+  issue(0, sA0, sB0, sS0);
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_vmem();
     __syncthreads();
+    const bool odd = kt & 1;
+    step(kt, kt + 1 < KT, odd ? sA0 : sA1, odd ? sB0 : sB1, odd ? sS0 : sS1,
+         odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sS1 : sS0);
   }
 
-  // ---- epilogue: (+ bias) -> 16-bit, MFMA layout: lane holds rows 4g..4g+3
-  // of a 16 x 16 block at column r16
+  // ---- epilogue: lane holds D[row, n .. n+3], row = block row r16
   const bool bf16 = p.out_bf16 != 0;
-  uint16_t* D = static_cast<uint16_t*>(p.D);
+  const bool vec = p.d_vec4 != 0;
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int64_t col = n0 + wn * TN + j * 16 + r16;
-    if (col >= N) continue;
-    const float bv = p.bias ? load_out_f32(p.bias, col, bf16) : 0.0f;
+  for (int i = 0; i < FM; ++i) {
+    const int64_t slot = m_lo + wm * TM + i * 16 + r16;
+    if (slot >= m_hi) continue;
+    int64_t drow = slot;
+    if constexpr (GROUPED) {
+      drow = p.c_inv ? (int64_t)p.c_inv[slot] : slot;
+      if (drow < 0 || drow >= p.M) continue;  // c_map was not a permutation
+    }
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int64_t slot = m_lo + wm * TM + i * 16 + 4 * g + rr;
-        if (slot >= m_hi) continue;
-        int64_t drow = slot;
-        if constexpr (GROUPED) {
-          drow = p.c_inv ? (int64_t)p.c_inv[slot] : slot;
-          if (drow < 0 || drow >= p.M) continue;  // c_map was not a permutation
-        }
-        D[drow * N + col] = to_out_bits(acc[i][j][rr] + bv, bf16);
-      }
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = n0 + wn * TN + j * 16 + 4 * g;
+      if (n >= N) continue;
+      store4(p, drow, n, acc[i][j], bf16, vec);
     }
   }
 }
@@ -428,6 +502,105 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny(TileParams p) {
 }
 
 // ------------------------------------------------------------------------------
+// Streaming (decode) kernel: K a multiple of 128
+// ------------------------------------------------------------------------------
+__device__ __forceinline__ i32x8 gload32(const uint8_t* p) {
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 16);
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// One workgroup per 16 weight rows (x one 16*MT-row activation block); its
+// NW waves split the 128-byte K chunks and issue every load of their share
+// before any math, so the whole weight slice is in flight at once. Lane group
+// g of both operands holds bytes [32g, 32g+32) of a chunk — exactly one
+// 32-wide K block — so for bk = 32 each block's partial sum is the
+// 16x16x128 product with the activation fragment zeroed outside lane group s
+// (compute is idle at decode sizes; the weight bytes are read once, 32 per
+// lane per chunk). Partials are summed over the waves in a fixed order.
+template <int KS, int MT, int NW, int R>
+__global__ __launch_bounds__(NW * 64) void gemm_stream(TileParams p) {
+  constexpr int KSUB = 128 / KS;
+  static_assert(R * KSUB <= 64, "round scales must fit one wave");
+  __shared__ f32x4 red[NW][MT][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t N = p.N, K = p.K, M = p.M;
+  const int KB = p.KB;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t m_base = (int64_t)blockIdx.y * (MT * 16);
+  const int NC = (int)(K / 128);
+  const int c_b = (int)((int64_t)w * NC / NW), c_e = (int)((int64_t)(w + 1) * NC / NW);
+
+  const int64_t nrow = n0 + r16 < N ? n0 + r16 : N - 1;
+  const uint8_t* wp = p.W + nrow * K + 32 * g;
+  const uint8_t* ap[MT];
+  const float* asp[MT];
+#pragma unroll
+  for (int mb = 0; mb < MT; ++mb) {
+    const int64_t m = m_base + mb * 16 + r16 < M ? m_base + mb * 16 + r16 : M - 1;
+    ap[mb] = p.A + m * K + 32 * g;
+    asp[mb] = p.As + m * KB;
+  }
+  const float* wsp = p.Ws + (n0 / p.bn) * KB;  // n0, bn multiples of 16: one block
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mb = 0; mb < MT; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const i32x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+
+  for (int c0 = c_b; c0 < c_e; c0 += R) {
+    i32x8 wf[R], af[R][MT];
+    float sa[R][KSUB][MT];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int c = c0 + u < c_e ? c0 + u : c_e - 1;
+      wf[u] = gload32(wp + (int64_t)c * 128);
+#pragma unroll
+      for (int mb = 0; mb < MT; ++mb) {
+        af[u][mb] = gload32(ap[mb] + (int64_t)c * 128);
+#pragma unroll
+        for (int s = 0; s < KSUB; ++s) sa[u][s][mb] = asp[mb][c * KSUB + s];
+      }
+    }
+    // this round's weight scales, one per lane, broadcast with readlane
+    const int kb_l = c0 * KSUB + lane < KB ? c0 * KSUB + lane : KB - 1;
+    const float wsl = wsp[kb_l];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      if (c0 + u >= c_e) break;
+#pragma unroll
+      for (int s = 0; s < KSUB; ++s) {
+        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsl), u * KSUB + s));
+#pragma unroll
+        for (int mb = 0; mb < MT; ++mb) {
+          const i32x8 a = (KS == 128 || g == s) ? af[u][mb] : zero8;
+          const f32x4 pr = mfma_fp8_k128(wf[u], a);
+          acc[mb] = fma4s(pr, sa[u][s][mb] * ws, acc[mb]);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int mb = 0; mb < MT; ++mb) red[w][mb][lane] = acc[mb];
+  __syncthreads();
+  const bool bf16 = p.out_bf16 != 0;
+  const bool vec = p.d_vec4 != 0;
+  for (int idx = tid; idx < MT * 64; idx += NW * 64) {
+    const int mb = idx >> 6, l2 = idx & 63;
+    const int64_t m = m_base + mb * 16 + (l2 & 15);
+    if (m >= M) continue;
+    f32x4 sum = red[0][mb][l2];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) sum += red[ww][mb][l2];
+    const int64_t n = n0 + 4 * (l2 >> 4);
+    if (n < N) store4(p, m, n, sum, bf16, vec);
+  }
+}
+
+// ------------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------------
 constexpr int kSkinnyMaxM = 64;
@@ -454,14 +627,43 @@ hipError_t launch_skinny(const TileParams& tp, hipStream_t st) {
   }
 }
 
+template <int KS, int MT>
+hipError_t launch_stream_mt(const TileParams& tp, hipStream_t st) {
+  constexpr int NW = 16;
+  constexpr int R = MT == 1 ? 4 : 2;
+  const int64_t gy = (tp.M + MT * 16 - 1) / (MT * 16);
+  if (gy > 65535 || (tp.N + 15) / 16 > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)((tp.N + 15) / 16), (unsigned)gy);
+  hipLaunchKernelGGL((gemm_stream<KS, MT, NW, R>), grid, dim3(NW * 64), 0, st, tp);
+  return hipGetLastError();
+}
+
+template <int KS>
+hipError_t launch_stream(const TileParams& tp, hipStream_t st) {
+  const int64_t mt = (tp.M + 15) / 16;
+  switch (mt) {
+    case 1: return launch_stream_mt<KS, 1>(tp, st);
+    case 2: return launch_stream_mt<KS, 2>(tp, st);
+    case 3: return launch_stream_mt<KS, 3>(tp, st);
+    default: return launch_stream_mt<KS, 4>(tp, st);
+  }
+}
+
 constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 4;
 
 template <int KS, bool GROUPED>
 hipError_t launch_tile(const TileParams& tp, int64_t tiles, hipStream_t st) {
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED>), dim3((unsigned)tiles),
-                     dim3(kWM * kWN * 64), 0, st, tp);
+  constexpr int TN = kBN / kWN;
+  // every 16-column block of a wave shares one weight-scale block when the
+  // wave's column range never crosses a bn boundary
+  const bool wsu = tp.bn % TN == 0;
+  const dim3 grid((unsigned)tiles), block(kWM * kWN * 64);
+  if (wsu)
+    hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED, true>), grid, block, 0, st, tp);
+  else
+    hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED, false>), grid, block, 0, st, tp);
   return hipGetLastError();
 }
 
@@ -474,6 +676,7 @@ TileParams make_params(const BlockGemmArgs& a) {
   tp.bn = a.bn;
   tp.nbw = (int)((a.N + a.bn - 1) / a.bn);
   tp.out_bf16 = a.out_dtype == Q8_BF16;
+  tp.d_vec4 = a.N % 4 == 0 && (uintptr_t)a.D % 8 == 0 && (uintptr_t)a.bias % 8 == 0;
   tp.tiles_n = (a.N + kBN - 1) / kBN;
   tp.tiles_m = (a.M + kBM - 1) / kBM;
   tp.offsets = a.expert_offsets; tp.a_map = a.a_map; tp.c_inv = a.c_inv; tp.E = a.E;
@@ -491,9 +694,10 @@ __global__ void invert_permutation(const int32_t* __restrict__ perm, int64_t n,
 hipError_t launch_blockwise(const BlockGemmArgs& a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   const TileParams tp = make_params(a);
-  // decode-sized M, or a K that is not a whole number of 128-byte slabs
-  if (a.M <= kSkinnyMaxM || a.K % 128 != 0)
+  if (a.K % 128 != 0)  // only the 8-byte-fragment kernel handles partial slabs
     return a.bk == 128 ? launch_skinny<128>(tp, st) : launch_skinny<32>(tp, st);
+  if (a.M <= kSkinnyMaxM)
+    return a.bk == 128 ? launch_stream<128>(tp, st) : launch_stream<32>(tp, st);
   const int64_t tiles = tp.tiles_m * tp.tiles_n;
   return a.bk == 128 ? launch_tile<128, false>(tp, tiles, st) : launch_tile<32, false>(tp, tiles, st);
 }
