@@ -11,9 +11,10 @@
 //                   chunk's per-expert histogram in LDS (counts are order
 //                   independent);
 //   2. moe_scan   — one thread per expert scans its counts over the chunks
-//                   (exclusive), then the per-expert totals are scanned over
-//                   the experts into expert_offsets and problem sizes, and the
-//                   chunk bases are shifted by the expert offsets;
+//                   (exclusive, from LDS slabs), then the per-expert totals
+//                   are scanned over the experts into expert_offsets and
+//                   problem sizes, and the chunk bases are shifted by the
+//                   expert offsets;
 //   3. moe_scatter — each entry's slot = its chunk's base for its expert plus
 //                   the number of earlier entries of the same expert inside
 //                   the chunk (counted from an LDS copy of the chunk), so
@@ -39,20 +40,36 @@ __global__ __launch_bounds__(kChunk) void moe_count(const int32_t* __restrict__ 
   for (int e = threadIdx.x; e < E; e += kChunk) counts[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
+// Chunk counts are staged through LDS a slab at a time (coalesced loads by
+// every thread) so that each expert's thread scans from LDS instead of
+// chasing dependent global loads.
+constexpr int kSlabInts = 8192;  // 32 KB of LDS
+
 __global__ __launch_bounds__(kScanThreads) void moe_scan(int32_t* __restrict__ counts,
                                                          int64_t nchunks, int E, int64_t nk,
                                                          int64_t kk, int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ ps1,
                                                          int32_t* __restrict__ ps2) {
   __shared__ int32_t tot[kScanThreads];
+  __shared__ int32_t slab[kSlabInts];
   const int e = threadIdx.x;
+  const int64_t rows_per_slab = kSlabInts / E;
   int32_t run = 0;
-  if (e < E) {
-    for (int64_t c = 0; c < nchunks; ++c) {
-      const int32_t v = counts[c * E + e];
-      counts[c * E + e] = run;
-      run += v;
+  // pass 1: per-expert exclusive scan over the chunks (relative bases)
+  for (int64_t c0 = 0; c0 < nchunks; c0 += rows_per_slab) {
+    const int64_t rows = nchunks - c0 < rows_per_slab ? nchunks - c0 : rows_per_slab;
+    for (int64_t i = threadIdx.x; i < rows * E; i += kScanThreads) slab[i] = counts[c0 * E + i];
+    __syncthreads();
+    if (e < E) {
+      for (int64_t r = 0; r < rows; ++r) {
+        const int32_t v = slab[r * E + e];
+        slab[r * E + e] = run;
+        run += v;
+      }
     }
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < rows * E; i += kScanThreads) counts[c0 * E + i] = slab[i];
+    __syncthreads();
   }
   tot[e] = e < E ? run : 0;
   __syncthreads();
@@ -69,8 +86,12 @@ __global__ __launch_bounds__(kScanThreads) void moe_scan(int32_t* __restrict__ c
     if (e == E - 1) offsets[E] = tot[e];
     ps1[3 * e + 0] = run; ps1[3 * e + 1] = (int32_t)nk; ps1[3 * e + 2] = (int32_t)kk;
     ps2[3 * e + 0] = run; ps2[3 * e + 1] = (int32_t)kk; ps2[3 * e + 2] = (int32_t)nk;
-    for (int64_t c = 0; c < nchunks; ++c) counts[c * E + e] += base;
   }
+  __shared__ int32_t base_of[kScanThreads];
+  if (e < E) base_of[e] = tot[e] - run;
+  __syncthreads();
+  // pass 2: shift every chunk base by its expert's offset (coalesced)
+  for (int64_t i = threadIdx.x; i < nchunks * E; i += kScanThreads) counts[i] += base_of[i % E];
 }
 
 __global__ __launch_bounds__(kChunk) void moe_scatter(const int32_t* __restrict__ ids, int64_t n,
