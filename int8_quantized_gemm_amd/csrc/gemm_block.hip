@@ -44,6 +44,7 @@ struct TileParams {
   int nbw;        // ceil(N / bn): weight-scale rows (per expert)
   int out_bf16;
   int d_vec4;     // N % 4 == 0 and D (and bias) 8-byte aligned: 8-byte stores
+  uint32_t a_bytes, as_bytes;  // extents of A and As (buffer resources)
   int64_t tiles_m, tiles_n;
   // expert-grouped variant
   const int32_t* offsets;  // [E+1] slot ranges per expert
@@ -107,9 +108,27 @@ __device__ __forceinline__ void g2l4(const void* g, void* lds) {
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Raw buffer resource over [base, base + bytes) and buffer -> LDS loads:
+// a 32-bit per-lane offset (VGPR) plus a wave-uniform offset (SGPR); lane l
+// writes lds + 16*l (or 4*l). Out-of-range lanes read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void b2l16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (Q8_AS3 void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void b2l4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (Q8_AS3 void*)lds, 4, voff, soff, 0, 0);
+}
+
+// 32-byte MFMA fragment of one row for lane group g: 16-byte chunks g and
+// g + 4 of the row's 128-byte K slab. Any assignment of K bytes to lane groups
+// gives the same product as long as both operands use it; this one makes the
+// sixteen rows x four lane groups of a ds_read_b128 conflict free (measured on
+// gfx950 with the swizzle of tile_common.h).
 __device__ __forceinline__ i32x8 lds_frag32(const uint8_t* base, int row, int g) {
-  const i32x4 lo = *reinterpret_cast<const i32x4*>(base + swz(row, 2 * g));
-  const i32x4 hi = *reinterpret_cast<const i32x4*>(base + swz(row, 2 * g + 1));
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(base + swz(row, g));
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(base + swz(row, g + 4));
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -169,8 +188,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * 128];
-  // activation scales of a stage, [KSUB][WM][16][FM]: a lane's FM row-block
-  // scales are contiguous
+  // activation scales of a stage, [KSUB][WM][FM/4][16][4]: a lane reads its FM
+  // row-block scales as FM/4 16-byte vectors, consecutive lanes 16 bytes apart
+  // (conflict free)
   __shared__ __attribute__((aligned(16))) float sS0[KSUB * BM];
   __shared__ __attribute__((aligned(16))) float sS1[KSUB * BM];
 
@@ -222,54 +242,73 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
   // ---- per-lane global sources of this wave's LDS loads. Wave load q of a
   // stage fills rows 8q..8q+7; lane l writes physical chunk l%8 of row
   // 8q + l/8, which holds logical chunk (l%8) ^ (row%8).
-  // 32-bit byte offsets from uniform bases (the host guarantees every operand
-  // is below 4 GiB), so each load is a scalar base + one VGPR
-  uint32_t a_off[A_PER], b_off[B_PER], s_off[S_PER];
+  // 32-bit byte offsets into buffer resources (the host guarantees every
+  // operand is below 4 GiB). Wave load q of a stage fills rows 8q..8q+7;
+  // lane l writes physical chunk l%8 of row 8q + l/8, which holds logical
+  // chunk (l%8) ^ swz_key(row), and swz_key(8q + l/8) = (4q + l/16) % 8
+  // depends on q only through its parity, which is the wave's parity (NW is
+  // even): one lane offset serves every load of the wave. The q and stage
+  // parts of the offset are scalars. Rows past the end of A or W fall
+  // outside the buffer and read as zeros (never stored).
+  static_assert(NW % 2 == 0, "wave count must be even");
+  const uint32_t lane_off =
+      (uint32_t)((lane >> 3) * K + (((lane & 7) ^ ((4 * (w & 1) + (lane >> 4)) & 7)) << 4));
+  uint32_t a_off[GROUPED ? A_PER : 1];
+  if constexpr (GROUPED) {
 #pragma unroll
-  for (int c = 0; c < A_PER; ++c) {
-    const int q = w + c * NW < A_SLOTS ? w + c * NW : 0;
-    const int row = 8 * q + (lane >> 3), lch = (lane & 7) ^ (row & 7);
-    a_off[c] = (uint32_t)(a_row(m_lo + row) * K + lch * 16);
+    for (int c = 0; c < A_PER; ++c) {
+      const int q = w + c * NW < A_SLOTS ? w + c * NW : 0;
+      const int row = 8 * q + (lane >> 3), lch = (lane & 7) ^ swz_key(row);
+      a_off[c] = (uint32_t)(a_row(m_lo + row) * K + lch * 16);
+    }
   }
-#pragma unroll
-  for (int c = 0; c < B_PER; ++c) {
-    const int q = w + c * NW < B_SLOTS ? w + c * NW : 0;
-    const int row = 8 * q + (lane >> 3), lch = (lane & 7) ^ (row & 7);
-    const int64_t n = n0 + row < N ? n0 + row : N - 1;
-    b_off[c] = (uint32_t)(n * K + lch * 16);
-  }
+  uint32_t s_off[S_PER];
+  // scale loads: waves past the last slot repeat an earlier slot (same bytes
+  // to the same place), so every wave issues the same instruction stream
 #pragma unroll
   for (int c = 0; c < S_PER; ++c) {
-    const int q = w + c * NW < S_SLOTS ? w + c * NW : 0;
+    const int q = (w + c * NW) % S_SLOTS;
     const int f = 64 * q + lane;
     const int s = f / BM, rem = f % BM;
     const int wmm = rem / TM, r2 = rem % TM;
-    const int row = wmm * TM + (r2 % FM) * 16 + r2 / FM;
+    const int quad = r2 >> 2, i = (quad >> 4) * 4 + (r2 & 3), rr = quad & 15;
+    const int row = wmm * TM + i * 16 + rr;
     s_off[c] = (uint32_t)((a_row(m_lo + row) * KB + s) * 4);
   }
-  const uint8_t* As_bytes = reinterpret_cast<const uint8_t*>(p.As);
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, p.a_bytes);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(Wb, (uint32_t)(N * K));
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(p.As, p.as_bytes);
+  const uint32_t a_base = GROUPED ? 0u : (uint32_t)(m_lo * K);
+  const uint32_t b_base = (uint32_t)(n0 * K);
   auto issue = [&](int kt, uint8_t* __restrict__ la, uint8_t* __restrict__ lb, float* __restrict__ ls) {
-    const uint8_t* ab = p.A + kt * 128;
-    const uint8_t* bb = Wb + kt * 128;
-    const uint8_t* sb = As_bytes + kt * KSUB * 4;
 #pragma unroll
-    for (int c = 0; c < A_PER; ++c)
-      if (A_SLOTS % NW == 0 || w + c * NW < A_SLOTS) g2l16(ab + a_off[c], la + (w + c * NW) * 1024);
+    for (int c = 0; c < A_PER; ++c) {
+      const int q = w + c * NW;
+      if (A_SLOTS % NW == 0 || q < A_SLOTS) {
+        if constexpr (GROUPED)
+          b2l16(rA, a_off[c], kt * 128, la + q * 1024);
+        else
+          b2l16(rA, lane_off, a_base + (uint32_t)(8 * q) * (uint32_t)K + kt * 128, la + q * 1024);
+      }
+    }
 #pragma unroll
-    for (int c = 0; c < B_PER; ++c)
-      if (B_SLOTS % NW == 0 || w + c * NW < B_SLOTS) g2l16(bb + b_off[c], lb + (w + c * NW) * 1024);
+    for (int c = 0; c < B_PER; ++c) {
+      const int q = w + c * NW;
+      if (B_SLOTS % NW == 0 || q < B_SLOTS)
+        b2l16(rB, lane_off, b_base + (uint32_t)(8 * q) * (uint32_t)K + kt * 128, lb + q * 1024);
+    }
 #pragma unroll
-    for (int c = 0; c < S_PER; ++c)
-      if (S_SLOTS % NW == 0 || w + c * NW < S_SLOTS) g2l4(sb + s_off[c], ls + (w + c * NW) * 64);
+    for (int c = 0; c < S_PER; ++c) b2l4(rS, s_off[c], kt * KSUB * 4, ls + ((w + c * NW) % S_SLOTS) * 64);
   };
 
-  // weight-scale rows of this wave's 16-column blocks (clamped for ragged N)
-  const float* ws_row[FN];
+  // weight-scale rows of this wave's 16-column blocks (clamped for ragged N);
+  // wave-uniform, kept in scalar registers
+  int ws_idx[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     int64_t nb = (n0 + wn * TN + j * 16) / p.bn;
     if (nb > p.nbw - 1) nb = p.nbw - 1;
-    ws_row[j] = Wsb + nb * KB;
+    ws_idx[j] = __builtin_amdgcn_readfirstlane((int)(nb * KB));
   }
 
   f32x4 acc[FM][FN];
@@ -286,7 +325,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
 #pragma unroll
     for (int s = 0; s < KSUB; ++s)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) wsv[s][j] = (WSU && j > 0) ? 0.0f : ws_row[j][kt * KSUB + s];
+      for (int j = 0; j < FN; ++j) wsv[s][j] = (WSU && j > 0) ? 0.0f : Wsb[ws_idx[j] + kt * KSUB + s];
   };
   auto compute = [&](const uint8_t* la, const uint8_t* lb, const float* ls, const float (&wv)[KSUB][FN]) {
 #pragma unroll
@@ -297,22 +336,34 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
       float sa[FM];
 #pragma unroll
       for (int i4 = 0; i4 < FM / 4; ++i4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(ls + s * BM + wm * TM + r16 * FM + 4 * i4);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ls + s * BM + wm * TM + (i4 * 16 + r16) * 4);
         sa[4 * i4] = v[0]; sa[4 * i4 + 1] = v[1]; sa[4 * i4 + 2] = v[2]; sa[4 * i4 + 3] = v[3];
       }
       if constexpr (KS == 128) {
+        // Software pipeline over the FM row blocks: the next activation
+        // fragment is read from LDS while this block's MFMAs run, and the
+        // MFMA results of block i are folded into the accumulators only after
+        // block i+1's MFMAs are issued (hides the MFMA result latency).
         i32x8 bw[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j) bw[j] = lds_frag32(lb, wn * TN + j * 16 + r16, g);
+        i32x8 av[2];
+        f32x4 pr[2][FN];
+        av[0] = lds_frag32(la, wm * TM + r16, g);
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          const i32x8 av = lds_frag32(la, wm * TM + i * 16 + r16, g);
-          f32x4 pr[FN];
+          if (i + 1 < FM) av[(i + 1) & 1] = lds_frag32(la, wm * TM + (i + 1) * 16 + r16, g);
 #pragma unroll
-          for (int j = 0; j < FN; ++j) pr[j] = mfma_fp8_k128(bw[j], av);
+          for (int j = 0; j < FN; ++j) pr[i & 1][j] = mfma_fp8_k128(bw[j], av[i & 1]);
+          if (i > 0) {
 #pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = fma4s(pr[j], sa[i] * ws[j], acc[i][j]);
+            for (int j = 0; j < FN; ++j)
+              acc[i - 1][j] = fma4s(pr[(i - 1) & 1][j], sa[i - 1] * ws[j], acc[i - 1][j]);
+          }
         }
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[FM - 1][j] = fma4s(pr[(FM - 1) & 1][j], sa[FM - 1] * ws[j], acc[FM - 1][j]);
       } else {
         long bw[FN];
 #pragma unroll
@@ -677,6 +728,11 @@ TileParams make_params(const BlockGemmArgs& a) {
   tp.nbw = (int)((a.N + a.bn - 1) / a.bn);
   tp.out_bf16 = a.out_dtype == Q8_BF16;
   tp.d_vec4 = a.N % 4 == 0 && (uintptr_t)a.D % 8 == 0 && (uintptr_t)a.bias % 8 == 0;
+  // A / As extents: the dense call knows M; the grouped call addresses A rows
+  // through a_map, so the extent is only bounded by the 4 GiB limit
+  const bool dense = a.expert_offsets == nullptr;
+  tp.a_bytes = dense ? (uint32_t)(a.M * a.K) : 0xFFFFFFFFu;
+  tp.as_bytes = dense ? (uint32_t)(a.M * (a.K / a.bk) * 4) : 0xFFFFFFFFu;
   tp.tiles_n = (a.N + kBN - 1) / kBN;
   tp.tiles_m = (a.M + kBM - 1) / kBM;
   tp.offsets = a.expert_offsets; tp.a_map = a.a_map; tp.c_inv = a.c_inv; tp.E = a.E;

@@ -1,17 +1,22 @@
 // Shared pieces of the LDS-tiled MFMA GEMM kernels (FP8 block-scaled and INT8).
 //
 // LDS tile layout: a [rows x 128 B] K-slab per stage, one 128-byte line per
-// row, split into eight 16-byte chunks. Chunk c of row r is stored at chunk
-// position c ^ (r & 7), so eight lanes reading the same logical chunk of eight
-// consecutive rows hit eight different 16-byte bank groups (no conflicts for
-// ds_read_b128), and the row-contiguous global loads stay fully coalesced.
+// row, split into eight 16-byte chunks. The LDS serves 256 bytes (64 banks of
+// 4 bytes) per cycle, so a pair of rows spans the banks once: an even row
+// sits in the lower 128 bytes of the bank space and an odd row in the upper.
+// Chunk c of row r is stored at chunk position c ^ ((r >> 1) & 7); sixteen
+// lanes reading the same logical chunk of sixteen consecutive rows then hit
+// sixteen different 16-byte bank groups (conflict-free ds_read_b128, and
+// ds_read_b64 of either half), while the row-contiguous global loads stay
+// fully coalesced.
 #pragma once
 
 #include "q8_device.h"
 
 namespace q8 {
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ swz_key(row)) << 4); }
 
 // Blocks of a launch are spread round-robin over the 8 XCDs (each with its
 // own L2). Renumber them so that consecutive logical tiles land on the same
