@@ -111,7 +111,8 @@ int quant_8bit(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, int64_t ld
  * W   [N, K] e4m3fn, Ws [ceil(N/bn), K/bk] float32.
  * bias [N] of out_dtype, or NULL.   D [M, N] of out_dtype (Q8_BF16, Q8_F16).
  * Rules: bk in {32, 128}; bn a positive multiple of 16; K % bk == 0
- * (ragged K is rejected, as the vLLM XPU kernel does); any M >= 0, N >= 1.
+ * (ragged K is rejected, as the vLLM XPU kernel does); any M >= 0, N >= 1;
+ * A, W and As each below 4 GiB (Q8_EUNSUPPORTED otherwise).
  * Accumulation: FP8 products summed in float32 per K block, scaled and
  * summed in float32.
  * workspace: blockwise_scaled_mm_workspace_size() bytes (0 today; reserved
@@ -136,7 +137,7 @@ int blockwise_scaled_mm(const void* A, const float* As, const void* W, const flo
  *   (+ (float)bias[n]) in float32 without contraction, then RNE.
  *   sa_numel in {1, M}, sb_numel in {1, N}; all four combinations broadcast.
  * out_dtype Q8_I32: D receives acc itself; sa, sb and bias must be NULL.
- * Rules: N % 16 == 0, K % 16 == 0, K <= 131071.
+ * Rules: N % 16 == 0, K % 16 == 0, K <= 131071, A and W each below 4 GiB.
  */
 int scaled_mm_int8(const int8_t* A, const float* sa, int64_t sa_numel,
                    const int8_t* W, const float* sb, int64_t sb_numel,

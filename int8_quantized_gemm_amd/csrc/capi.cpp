@@ -33,6 +33,7 @@ int hip_status(hipError_t e, const char* what) {
 bool is_16bit_out(q8_dtype t) { return t == Q8_BF16 || t == Q8_F16; }
 
 constexpr int64_t kMaxI32 = 0x7FFFFFFFLL;
+constexpr int64_t kFourGiB = 0x100000000LL;
 
 // Shared validation of the block-scaled FP8 GEMM shape rules.
 int check_block_shape(const char* fn, int64_t M, int64_t N, int64_t K, int bn, int bk) {
@@ -43,6 +44,9 @@ int check_block_shape(const char* fn, int64_t M, int64_t N, int64_t K, int bn, i
   if (K % bk != 0) return fail(Q8_ESHAPE, "%s: K (%lld) must be a multiple of bk (%d)", fn, (long long)K, bk);
   if (K / bk > kMaxI32 || (N + bn - 1) / bn > kMaxI32)
     return fail(Q8_ESHAPE, "%s: too many blocks", fn);
+  // the kernels address every operand with 32-bit byte offsets
+  if (M * K >= kFourGiB || N * K >= kFourGiB || M * (K / bk) * 4 >= kFourGiB)
+    return fail(Q8_EUNSUPPORTED, "%s: an operand (A, W or As) reaches 4 GiB", fn);
   return Q8_OK;
 }
 
@@ -131,6 +135,8 @@ int scaled_mm_int8(const int8_t* A, const float* sa, int64_t sa_numel, const int
     return fail(Q8_ESHAPE, "%s: N (%lld) and K (%lld) must be multiples of 16", fn, (long long)N,
                 (long long)K);
   if (K > 131071) return fail(Q8_ESHAPE, "%s: K above 131071 could overflow int32", fn);
+  if (M * K >= kFourGiB || N * K >= kFourGiB)
+    return fail(Q8_EUNSUPPORTED, "%s: an operand (A or W) reaches 4 GiB", fn);
   if (out_dtype == Q8_I32) {
     if (sa || sb || bias) return fail(Q8_EINVAL, "%s: I32 output takes no scales and no bias", fn);
   } else {

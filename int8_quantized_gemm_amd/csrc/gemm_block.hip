@@ -95,32 +95,6 @@ __device__ __forceinline__ uint16_t to_out_bits(float v, bool bf16) {
 // ------------------------------------------------------------------------------
 // LDS-tiled kernel
 // ------------------------------------------------------------------------------
-#define Q8_AS1 __attribute__((address_space(1)))
-#define Q8_AS3 __attribute__((address_space(3)))
-
-// Direct global -> LDS loads (no staging registers): lane l of the wave writes
-// its 16 (or 4) bytes at lds + 16*l (4*l); lds must be wave-uniform.
-__device__ __forceinline__ void g2l16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((Q8_AS1 void*)g, (Q8_AS3 void*)lds, 16, 0, 0);
-}
-__device__ __forceinline__ void g2l4(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((Q8_AS1 void*)g, (Q8_AS3 void*)lds, 4, 0, 0);
-}
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Raw buffer resource over [base, base + bytes) and buffer -> LDS loads:
-// a 32-bit per-lane offset (VGPR) plus a wave-uniform offset (SGPR); lane l
-// writes lds + 16*l (or 4*l). Out-of-range lanes read zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ void b2l16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (Q8_AS3 void*)lds, 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void b2l4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (Q8_AS3 void*)lds, 4, voff, soff, 0, 0);
-}
-
 // 32-byte MFMA fragment of one row for lane group g: 16-byte chunks g and
 // g + 4 of the row's 128-byte K slab. Any assignment of K bytes to lane groups
 // gives the same product as long as both operands use it; this one makes the
@@ -253,15 +227,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
   static_assert(NW % 2 == 0, "wave count must be even");
   const uint32_t lane_off =
       (uint32_t)((lane >> 3) * K + (((lane & 7) ^ ((4 * (w & 1) + (lane >> 4)) & 7)) << 4));
-  uint32_t a_off[GROUPED ? A_PER : 1];
+  // Grouped: the tile's gathered A rows differ per lane; their byte offsets
+  // live in a small LDS table read at every stage (kept in registers they
+  // would be spilled, and reloading a spill waits on every load in flight).
+  __shared__ uint32_t sAoff[GROUPED ? BM : 1];
   if constexpr (GROUPED) {
-#pragma unroll
-    for (int c = 0; c < A_PER; ++c) {
-      const int q = w + c * NW < A_SLOTS ? w + c * NW : 0;
-      const int row = 8 * q + (lane >> 3), lch = (lane & 7) ^ swz_key(row);
-      a_off[c] = (uint32_t)(a_row(m_lo + row) * K + lch * 16);
-    }
+    for (int r = tid; r < BM; r += NW * 64) sAoff[r] = (uint32_t)(a_row(m_lo + r) * K);
+    __syncthreads();
   }
+  const uint32_t chunk_off = lane_off - (uint32_t)((lane >> 3) * K);
   uint32_t s_off[S_PER];
   // scale loads: waves past the last slot repeat an earlier slot (same bytes
   // to the same place), so every wave issues the same instruction stream
@@ -286,7 +260,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
       const int q = w + c * NW;
       if (A_SLOTS % NW == 0 || q < A_SLOTS) {
         if constexpr (GROUPED)
-          b2l16(rA, a_off[c], kt * 128, la + q * 1024);
+          b2l16(rA, sAoff[8 * q + (lane >> 3)] + chunk_off, kt * 128, la + q * 1024);
         else
           b2l16(rA, lane_off, a_base + (uint32_t)(8 * q) * (uint32_t)K + kt * 128, la + q * 1024);
       }
@@ -333,12 +307,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
       float ws[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j) ws[j] = WSU ? wv[s][0] : wv[s][j];
-      float sa[FM];
-#pragma unroll
-      for (int i4 = 0; i4 < FM / 4; ++i4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(ls + s * BM + wm * TM + (i4 * 16 + r16) * 4);
-        sa[4 * i4] = v[0]; sa[4 * i4 + 1] = v[1]; sa[4 * i4 + 2] = v[2]; sa[4 * i4 + 3] = v[3];
-      }
+      // activation scales of four row blocks at a time (one 16-byte read)
+      auto sa_quad = [&](int i4) {
+        return *reinterpret_cast<const f32x4*>(ls + s * BM + wm * TM + (i4 * 16 + r16) * 4);
+      };
       if constexpr (KS == 128) {
         // Software pipeline over the FM row blocks: the next activation
         // fragment is read from LDS while this block's MFMAs run, and the
@@ -350,6 +322,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
         i32x8 av[2];
         f32x4 pr[2][FN];
         av[0] = lds_frag32(la, wm * TM + r16, g);
+        f32x4 saq = sa_quad(0);
+        float sa_prev = 0.0f;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           if (i + 1 < FM) av[(i + 1) & 1] = lds_frag32(la, wm * TM + (i + 1) * 16 + r16, g);
@@ -358,13 +332,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
           if (i > 0) {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-              acc[i - 1][j] = fma4s(pr[(i - 1) & 1][j], sa[i - 1] * ws[j], acc[i - 1][j]);
+              acc[i - 1][j] = fma4s(pr[(i - 1) & 1][j], sa_prev * ws[j], acc[i - 1][j]);
           }
+          sa_prev = saq[i & 3];
+          if ((i & 3) == 3 && i + 1 < FM) saq = sa_quad((i + 1) >> 2);
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[FM - 1][j] = fma4s(pr[(FM - 1) & 1][j], sa[FM - 1] * ws[j], acc[FM - 1][j]);
+          acc[FM - 1][j] = fma4s(pr[(FM - 1) & 1][j], sa_prev * ws[j], acc[FM - 1][j]);
       } else {
+        float sa[FM];
+#pragma unroll
+        for (int i4 = 0; i4 < FM / 4; ++i4) {
+          const f32x4 v = sa_quad(i4);
+          sa[4 * i4] = v[0]; sa[4 * i4 + 1] = v[1]; sa[4 * i4 + 2] = v[2]; sa[4 * i4 + 3] = v[3];
+        }
         long bw[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j) bw[j] = lds_frag8(lb, wn * TN + j * 16 + r16, s, g);

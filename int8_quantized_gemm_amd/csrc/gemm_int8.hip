@@ -9,7 +9,9 @@
 // matrix cores (v_mfma_i32_16x16x64_i8, chained), with no per-block work; the
 // scales and bias are applied once in the epilogue in float32 without FMA
 // contraction: ((float)acc * sa) * sb + bias, then round to nearest even.
-// Tiling, LDS layout and tile order are those of the FP8 tile kernel.
+// gemm_int8_pipe (K % 128 == 0) uses the FP8 tile kernel's pipeline;
+// gemm_int8_tile (register-staged loads, zero-filled partial last slab) covers
+// K % 128 != 0.
 #include "q8_internal.h"
 #include "tile_common.h"
 
@@ -157,6 +159,137 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_int8_tile(Int8Params p) 
   }
 }
 
+// K a multiple of 128: the FP8 tile kernel's pipeline (buffer -> LDS loads
+// with scalar stage offsets, two LDS stages, one barrier per 128-byte K slab,
+// conflict-free fragment layout) with the int32 accumulation kept inside the
+// matrix cores. MFMA operand 0 is the weight fragment, so a lane's four
+// accumulators are four consecutive output columns of one row.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_int8_pipe(Int8Params p) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int A_SLOTS = BM / 8, B_SLOTS = BN / 8;
+  constexpr int A_PER = (A_SLOTS + NW - 1) / NW, B_PER = (B_SLOTS + NW - 1) / NW;
+  static_assert(NW % 2 == 0 && TM % 16 == 0 && TN % 16 == 0, "tile");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * 128];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w / WN, wn = w % WN;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t M = p.M, N = p.N, K = p.K;
+
+  const int64_t t = xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n);
+  int64_t tm, tn;
+  grouped_order(t, p.tiles_m, p.tiles_n, 8, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+
+  // same load geometry as the FP8 tile kernel (rows past the end of A or W
+  // read zeros from the buffer resource and are never stored)
+  const uint32_t lane_off =
+      (uint32_t)((lane >> 3) * K + (((lane & 7) ^ ((4 * (w & 1) + (lane >> 4)) & 7)) << 4));
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (uint32_t)(M * K));
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.W, (uint32_t)(N * K));
+  const uint32_t a_base = (uint32_t)(m0 * K), b_base = (uint32_t)(n0 * K);
+  auto issue = [&](int kt, uint8_t* __restrict__ la, uint8_t* __restrict__ lb) {
+#pragma unroll
+    for (int c = 0; c < A_PER; ++c) {
+      const int q = w + c * NW;
+      if (A_SLOTS % NW == 0 || q < A_SLOTS)
+        b2l16(rA, lane_off, a_base + (uint32_t)(8 * q) * (uint32_t)K + kt * 128, la + q * 1024);
+    }
+#pragma unroll
+    for (int c = 0; c < B_PER; ++c) {
+      const int q = w + c * NW;
+      if (B_SLOTS % NW == 0 || q < B_SLOTS)
+        b2l16(rB, lane_off, b_base + (uint32_t)(8 * q) * (uint32_t)K + kt * 128, lb + q * 1024);
+    }
+  };
+
+  i32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+
+  // lane group g holds 16-byte chunks g (first 64-wide K step) and g + 4
+  // (second) of each row: the same K assignment for both operands
+  auto compute = [&](const uint8_t* la, const uint8_t* lb) {
+    i32x4 bw[2][FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int row = wn * TN + j * 16 + r16;
+      bw[0][j] = *reinterpret_cast<const i32x4*>(lb + swz(row, g));
+      bw[1][j] = *reinterpret_cast<const i32x4*>(lb + swz(row, g + 4));
+    }
+    i32x4 av[2][2];
+    av[0][0] = *reinterpret_cast<const i32x4*>(la + swz(wm * TM + r16, g));
+    av[0][1] = *reinterpret_cast<const i32x4*>(la + swz(wm * TM + r16, g + 4));
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (i + 1 < FM) {
+        const int row = wm * TM + (i + 1) * 16 + r16;
+        av[(i + 1) & 1][0] = *reinterpret_cast<const i32x4*>(la + swz(row, g));
+        av[(i + 1) & 1][1] = *reinterpret_cast<const i32x4*>(la + swz(row, g + 4));
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bw[h][j], av[i & 1][h], acc[i][j], 0, 0, 0);
+    }
+  };
+  auto step = [&](int kt, bool refill, uint8_t* __restrict__ na, uint8_t* __restrict__ nb,
+                  const uint8_t* __restrict__ la, const uint8_t* __restrict__ lb) {
+    if (refill) issue(kt + 1, na, nb);
+    compute(la, lb);
+  };
+  const int KT = (int)(K / 128);
+  issue(0, sA0, sB0);
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_vmem();
+    __syncthreads();
+    const bool odd = kt & 1;
+    step(kt, kt + 1 < KT, odd ? sA0 : sA1, odd ? sB0 : sB1, odd ? sA1 : sA0, odd ? sB1 : sB0);
+  }
+
+  // epilogue: lane holds D[m, n .. n+3]
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t m = m0 + wm * TM + i * 16 + r16;
+    if (m >= M) continue;
+    const float sav = p.out_kind != 0 ? p.sa[p.sa_per_row ? m : 0] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = n0 + wn * TN + j * 16 + 4 * g;
+      if (n >= N) continue;  // N % 16 == 0: n .. n+3 all in range otherwise
+      const i32x4 v = acc[i][j];
+      if (p.out_kind == 0) {
+        *reinterpret_cast<i32x4*>(static_cast<int32_t*>(p.D) + m * N + n) = v;
+      } else {
+        uint32_t o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float sbv = p.sb[p.sb_per_col ? n + r : 0];
+          float f = __fmul_rn(__fmul_rn((float)v[r], sav), sbv);
+          if (p.bias) {
+            const uint16_t hb = static_cast<const uint16_t*>(p.bias)[n + r];
+            f = __fadd_rn(f, p.out_kind == 1 ? bf16_bits_to_f32(hb) : f16_bits_to_f32(hb));
+          }
+          o[r] = p.out_kind == 1 ? f32_to_bf16_bits(f) : f32_to_f16_bits(f);
+        }
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.D) + m * N + n) =
+            uint2{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+      }
+    }
+  }
+}
+
 constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 4;
 
 }  // namespace
@@ -173,8 +306,15 @@ hipError_t launch_int8(const Int8GemmArgs& a, hipStream_t st) {
   p.tiles_n = (a.N + kBN - 1) / kBN;
   const int64_t tiles = p.tiles_m * p.tiles_n;
   if (tiles > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((gemm_int8_tile<kBM, kBN, kWM, kWN>), dim3((unsigned)tiles),
-                     dim3(kWM * kWN * 64), 0, st, p);
+  // the pipelined kernel needs whole 128-byte K slabs and 16-byte aligned rows
+  // of D (N % 16 == 0 always holds here)
+  const bool pipe = a.K % 128 == 0 && (uintptr_t)a.D % 16 == 0 && (uintptr_t)a.bias % 8 == 0;
+  if (pipe)
+    hipLaunchKernelGGL((gemm_int8_pipe<kBM, kBN, kWM, kWN>), dim3((unsigned)tiles),
+                       dim3(kWM * kWN * 64), 0, st, p);
+  else
+    hipLaunchKernelGGL((gemm_int8_tile<kBM, kBN, kWM, kWN>), dim3((unsigned)tiles),
+                       dim3(kWM * kWN * 64), 0, st, p);
   return hipGetLastError();
 }
 

@@ -18,6 +18,32 @@ namespace q8 {
 __device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ swz_key(row)) << 4); }
 
+#define Q8_AS1 __attribute__((address_space(1)))
+#define Q8_AS3 __attribute__((address_space(3)))
+
+// Direct global -> LDS loads (no staging registers): lane l of the wave writes
+// its 16 (or 4) bytes at lds + 16*l (4*l); lds must be wave-uniform.
+__device__ __forceinline__ void g2l16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((Q8_AS1 void*)g, (Q8_AS3 void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void g2l4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((Q8_AS1 void*)g, (Q8_AS3 void*)lds, 4, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Raw buffer resource over [base, base + bytes) and buffer -> LDS loads:
+// a 32-bit per-lane offset (VGPR) plus a wave-uniform offset (SGPR); lane l
+// writes lds + 16*l (or 4*l). Out-of-range lanes read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void b2l16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (Q8_AS3 void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void b2l4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (Q8_AS3 void*)lds, 4, voff, soff, 0, 0);
+}
+
 // Blocks of a launch are spread round-robin over the 8 XCDs (each with its
 // own L2). Renumber them so that consecutive logical tiles land on the same
 // XCD: block b runs on XCD b % 8, and logical ids are handed out to XCDs in
