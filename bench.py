@@ -294,6 +294,33 @@ class _Null:
         return False
 
 
+def traffic_probe(torch, q8, synth) -> int:
+    """Kernels for the HBM byte counters: three prefill GEMM launches (inputs
+    written fresh each time so they are not resident in the Infinity Cache)
+    and three plain 256 MiB device-to-device copies of known size (the scale
+    for FETCH_SIZE / WRITE_SIZE)."""
+    M, N, K, blk = 4096, 7168, 7168, 128
+    dev = "cuda:0"
+    x = synth.activations(M, K, "bf16", seed=0).to(dev)
+    Wq, Ws = synth.fp8_block_weights(N, K, blk, blk, seed=0)
+    Wq, Ws = Wq.to(dev), Ws.to(dev)
+    aq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+    As = torch.empty((M, K // blk), dtype=torch.float32, device=dev)
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    big = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+    src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
+    dst = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        q8.quant_8bit(x, aq, As, blk, EPS, -448.0, 448.0, False)
+        big.fill_(1)  # evict: 256 MiB written between launches
+        q8.blockwise_scaled_mm(aq, Wq, As, Ws, torch.bfloat16, block=(blk, blk), out=D)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("traffic probe done: 3 GEMM launches, 3 copies of 268435456 bytes")
+    return 0
+
+
 def cpu_baseline(pre, rows: int):
     """The oracle as it stands, on the first ``rows`` rows of the prefill
     workload: quantize those rows, then the block-scaled GEMM against all of W."""
@@ -318,7 +345,7 @@ def cpu_baseline(pre, rows: int):
     _ = np
     return {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s",
             "cores": threads or len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"prefill rows 0..{rows - 1} of {M} (quant + block GEMM, N={N}, K={K}), {dt:.2f} s"}
+            "sample": f"prefill rows 0..{rows - 1} of {M} (quant + block GEMM, N={N}, K={K}), {dt:.2f} s of CPU time"}
 
 
 def main() -> int:
@@ -326,7 +353,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-rows", type=int, default=512, help="prefill rows for the oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="prefill rows for the oracle baseline")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only run prefill GEMM launches and a 256 MiB device copy (for HBM counters)")
     ap.add_argument("--skip-secondary", action="store_true", help="headline prefill only")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -341,6 +370,8 @@ def main() -> int:
 
     torch.cuda.init()
     log(f"device {torch.cuda.get_device_name(0)}")
+    if args.traffic_probe:
+        return traffic_probe(torch, q8, synth)
     pre = bench_prefill(torch, q8, synth, args.steps, args.warmup)
     log(f"prefill: {pre['ms_per_step']:.3f} ms/step, GEMM {pre['gemm_us']['mean']:.1f} us "
         f"= {pre['gemm_tflops']:.0f} TFLOP/s")
