@@ -634,6 +634,117 @@ __global__ __launch_bounds__(NW * 64) void gemm_stream(TileParams p) {
 }
 
 // ------------------------------------------------------------------------------
+// Streaming (decode) kernel with shared activations: M <= 16, K a multiple of 1024
+// ------------------------------------------------------------------------------
+// Every workgroup needs all M activation rows and their scales. Read from L2
+// by every wave, those few lines are requested by thousands of waves at once
+// and serialise on their L2 channels; here one linear pass per workgroup
+// copies them into LDS (buffer->LDS, 1 KB per load) while the weight loads of
+// every wave are already in flight, and the waves read them from LDS.
+// LDS: activation rows at a pitch of K + 16 bytes (sixteen lanes reading one
+// K offset of sixteen rows hit sixteen bank groups), then the scale rows,
+// then the waves' partials.
+template <int KS, int NW, int R>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, NW / 4)))
+void gemm_stream_sa(TileParams p) {
+  constexpr int KSUB = 128 / KS;
+  static_assert(R * KSUB <= 64, "round scales must fit one wave");
+  static_assert(KSUB == 1 || KSUB == 4, "128- or 32-wide K blocks");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t N = p.N, K = p.K, M = p.M;  // M <= 16
+  const int KB = p.KB;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int NC = (int)(K / 128);
+  const int c_b = (int)((int64_t)w * NC / NW), c_e = (int)((int64_t)(w + 1) * NC / NW);
+  const uint32_t a_pitch = (uint32_t)K + 16;
+  const uint32_t s_bytes = (uint32_t)(M * KB * 4);
+  uint8_t* sA = smem;
+  uint8_t* sS = smem + M * a_pitch;
+  f32x4* red = reinterpret_cast<f32x4*>(sS + ((s_bytes + 1023u) & ~1023u));  // [NW][64]
+
+  // ---- activations and scales -> LDS (rows are K bytes, K a multiple of
+  // 1024, so no load crosses a row); the scale copy is rounded up to whole
+  // 1 KB loads, the tail reading zeros from the resource's range check
+  {
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (uint32_t)(M * K));
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(p.As, s_bytes);
+    const int per_row = (int)(K / 1024), a_loads = (int)M * per_row;
+    for (int i = w; i < a_loads; i += NW) {
+      const int row = i / per_row, col = (i - row * per_row) * 1024;
+      b2l16(rA, (uint32_t)lane * 16, (uint32_t)i * 1024, sA + row * a_pitch + col);
+    }
+    const int s_loads = (int)((s_bytes + 1023u) >> 10);
+    for (int i = w; i < s_loads; i += NW) b2l16(rS, (uint32_t)lane * 16, (uint32_t)i * 1024, sS + i * 1024);
+  }
+  // this wave's weight scales (one per lane) and weight chunks, issued after
+  // the LDS copies so that waiting for the copies leaves them in flight
+  const float* wsp = p.Ws + (n0 / p.bn) * KB;  // n0, bn multiples of 16: one block
+  const int kb_l = c_b * KSUB + lane < KB ? c_b * KSUB + lane : KB - 1;
+  const float wsl = wsp[kb_l];
+  asm volatile("" ::: "memory");
+  const int64_t nrow = n0 + r16 < N ? n0 + r16 : N - 1;
+  const uint8_t* wp = p.W + nrow * K + 32 * g;
+  i32x8 wf[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    // unconditional (clamped) loads: exactly 2R of them follow the copies
+    const int c = c_b + u < NC - 1 ? c_b + u : NC - 1;
+    wf[u] = gload32(wp + (int64_t)c * 128);
+  }
+  // the copies were issued before the 2R weight loads, and loads complete in
+  // order: at most 2R outstanding means this wave's copies have landed. The
+  // bare barrier (no fence) keeps the weight loads in flight across it.
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * R) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const i32x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int arow = r16 < M ? r16 : (int)M - 1;  // rows past M repeat the last (never stored)
+  const uint8_t* al = sA + arow * a_pitch + 32 * g;
+  const float* sl = reinterpret_cast<const float*>(sS) + arow * KB;
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int c = c_b + u;
+    if (c >= c_e) break;
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(al + c * 128);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(al + c * 128 + 16);
+    const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    f32x4 sa;
+    if constexpr (KSUB == 4) sa = *reinterpret_cast<const f32x4*>(sl + c * 4);
+    else sa[0] = sl[c];
+#pragma unroll
+    for (int s = 0; s < KSUB; ++s) {
+      const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsl), u * KSUB + s));
+      const i32x8 a = (KS == 128 || g == s) ? af : zero8;
+      const f32x4 pr = mfma_fp8_k128(wf[u], a);
+      acc = fma4s(pr, sa[s] * ws, acc);
+    }
+  }
+
+  red[w * 64 + lane] = acc;
+  __syncthreads();
+  // fixed-order sum over the waves, one output per thread
+  const bool bf16 = p.out_bf16 != 0;
+  uint16_t* D = static_cast<uint16_t*>(p.D);
+  const float* redf = reinterpret_cast<const float*>(red);
+  for (int idx = tid; idx < 256; idx += NW * 64) {
+    const int l2 = idx >> 2, rr = idx & 3;
+    const int64_t m = l2 & 15;
+    const int64_t n = n0 + 4 * (l2 >> 4) + rr;
+    if (m >= M || n >= N) continue;
+    float sum = redf[l2 * 4 + rr];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) sum += redf[(ww * 64 + l2) * 4 + rr];
+    if (p.bias) sum += load_out_f32(p.bias, n, bf16);
+    D[m * N + n] = to_out_bits(sum, bf16);
+  }
+}
+
+// ------------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------------
 constexpr int kSkinnyMaxM = 64;
@@ -668,6 +779,38 @@ hipError_t launch_stream_mt(const TileParams& tp, hipStream_t st) {
   if (gy > 65535 || (tp.N + 15) / 16 > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((tp.N + 15) / 16), (unsigned)gy);
   hipLaunchKernelGGL((gemm_stream<KS, MT, NW, R>), grid, dim3(NW * 64), 0, st, tp);
+  return hipGetLastError();
+}
+
+constexpr int64_t kLdsBytes = 160 * 1024;
+constexpr int kStreamSaNW = 16;
+constexpr int kStreamSaR = 4;
+
+// dynamic LDS of gemm_stream_sa
+inline int64_t stream_sa_lds(int64_t M, int64_t K, int KB) {
+  return M * (K + 16) + ((M * KB * 4 + 1023) & ~1023LL) + (int64_t)kStreamSaNW * 64 * 16;
+}
+
+// M <= 16, K a multiple of 1024, at most kStreamSaR chunks of 128 per wave,
+// and the staged activations fit in LDS
+inline bool stream_sa_fits(int64_t M, int64_t K, int KB) {
+  return M <= 16 && K % 1024 == 0 && (K / 128 + kStreamSaNW - 1) / kStreamSaNW <= kStreamSaR &&
+         stream_sa_lds(M, K, KB) <= kLdsBytes;
+}
+
+template <int KS>
+hipError_t launch_stream_sa(const TileParams& tp, hipStream_t st) {
+  const auto kern = gemm_stream_sa<KS, kStreamSaNW, kStreamSaR>;
+  static bool attr_set = false;  // raising the limit is idempotent
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  if ((tp.N + 15) / 16 > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  const unsigned lds = (unsigned)stream_sa_lds(tp.M, tp.K, tp.KB);
+  hipLaunchKernelGGL(kern, dim3((unsigned)((tp.N + 15) / 16)), dim3(kStreamSaNW * 64), lds, st, tp);
   return hipGetLastError();
 }
 
@@ -734,8 +877,17 @@ hipError_t launch_blockwise(const BlockGemmArgs& a, hipStream_t st) {
   const TileParams tp = make_params(a);
   if (a.K % 128 != 0)  // only the 8-byte-fragment kernel handles partial slabs
     return a.bk == 128 ? launch_skinny<128>(tp, st) : launch_skinny<32>(tp, st);
-  if (a.M <= kSkinnyMaxM)
+  // the streaming kernel reads a chunk's four 32-wide activation scales as
+  // one 16-byte vector
+  if (a.M <= kSkinnyMaxM) {
+    // from 8 activation rows on, staging them once per workgroup beats every
+    // wave reading them from L2 (measured: M = 16 12.2 -> 10.8 us, M = 1 and
+    // 4 slightly slower staged)
+    if (a.M >= 8 && stream_sa_fits(a.M, a.K, tp.KB) && (uintptr_t)a.A % 16 == 0 &&
+        (uintptr_t)a.As % 16 == 0)
+      return a.bk == 128 ? launch_stream_sa<128>(tp, st) : launch_stream_sa<32>(tp, st);
     return a.bk == 128 ? launch_stream<128>(tp, st) : launch_stream<32>(tp, st);
+  }
   const int64_t tiles = tp.tiles_m * tp.tiles_n;
   return a.bk == 128 ? launch_tile<128, false>(tp, tiles, st) : launch_tile<32, false>(tp, tiles, st);
 }

@@ -67,9 +67,19 @@ def test_tiny_fp32_block128():
     run_case(4, 256, 512, 128, 128, x_dtype="f32")
 
 
-@pytest.mark.parametrize("M", [1, 4, 16, 64])
+@pytest.mark.parametrize("M", [1, 4, 8, 12, 16, 64])
 def test_decode_block32_ue8m0(M):
     run_case(M, 4096, 7168, 32, 32, ue=True, outliers=0.01)
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 1000, 1024), (13, 520, 2048), (16, 4096, 8192),
+                                   (9, 48, 3072), (16, 16, 1024)])
+@pytest.mark.parametrize("bk", [128, 32])
+def test_decode_shared_activation_shapes(M, N, K, bk):
+    """8..16 activation rows with K a multiple of 1024 take the kernel that
+    stages the activations once per workgroup: waves without K chunks
+    (K = 1024), ragged N, the largest K it accepts (8192)."""
+    run_case(M, N, K, bk, bk, ue=(bk == 32), bias=True, seed=M * 7 + K)
 
 
 @pytest.mark.parametrize("N", [7168, 18432])
