@@ -53,15 +53,6 @@ struct TileParams {
   int E;
 };
 
-__device__ __forceinline__ f32x4 fma4(f32x4 p, f32x4 s, f32x4 acc) {
-  f32x4 r;
-  r[0] = __builtin_fmaf(p[0], s[0], acc[0]);
-  r[1] = __builtin_fmaf(p[1], s[1], acc[1]);
-  r[2] = __builtin_fmaf(p[2], s[2], acc[2]);
-  r[3] = __builtin_fmaf(p[3], s[3], acc[3]);
-  return r;
-}
-
 __device__ __forceinline__ f32x4 fma4s(f32x4 p, float s, f32x4 acc) {
   f32x4 r;
   r[0] = __builtin_fmaf(p[0], s, acc[0]);

@@ -90,6 +90,17 @@ def test_strided_input_rows():
     assert np.array_equal(sg, so) and np.array_equal(qg.view(np.uint8), qo)
 
 
+@pytest.mark.parametrize("g", [16, 128])
+def test_strided_rows_eight_element_lanes(g):
+    """A row stride of 1032 elements (a multiple of 8, not of 16) keeps the
+    kernel at 8 elements per lane for every group size."""
+    full = synth.activations(24, 1032, "bf16", seed=9)
+    x = full[:, :1024]
+    qg, sg = run_quant(full.to(DEV)[:, :1024], g)
+    qo, so = oracle_quant(x.contiguous(), g)
+    assert np.array_equal(sg, so) and np.array_equal(qg.view(np.uint8), qo)
+
+
 def test_cast_sweep_every_bf16_value():
     """Groups headed by 448 have scale 1, so the codes are the convert of every
     finite bf16 value in range: exercises subnormals, ties, signed zeros."""
