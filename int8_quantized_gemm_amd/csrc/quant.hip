@@ -18,8 +18,11 @@
 //                      loads 8 consecutive elements (16 B for bf16/f16), the
 //                      group's lanes are adjacent in one wave and reduce their
 //                      absolute maximum with xor shuffles. HBM-bound.
-//   quant_group_block  any group size (per-token rows, odd sizes, unaligned
-//                      strides): one workgroup per group, block reduction,
+//   quant_group_regs   groups of up to 8192 elements that are a multiple of 8
+//                      (per-token rows): one workgroup per group held in
+//                      registers, block reduction, codes.
+//   quant_group_block  any other group size (odd sizes, unaligned strides,
+//                      longer rows): one workgroup per group, block reduction,
 //                      then a second pass that re-reads the group (L2 hit).
 //   amax_partials +    per-tensor dynamic: per-workgroup maxima into the
 //   quant_tensor       workspace, then every workgroup reduces them (the max
@@ -275,6 +278,45 @@ __global__ __launch_bounds__(kThreads) void quant_group_block(
   }
 }
 
+// One workgroup per group of up to kThreads * 8 * NV elements (a per-token
+// row, say) held in registers: one read of the input, a block reduction, then
+// the codes, instead of re-reading the group after the reduction.
+template <int XT, bool FP8, bool UE, int NV>
+__global__ __launch_bounds__(kThreads) void quant_group_regs(
+    const void* __restrict__ x, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
+    float* __restrict__ s, int64_t g, float eps, float qmin, float qmax) {
+  __shared__ float red[kThreads / kWave];
+  const int64_t groups_per_row = K / g;
+  const int64_t row = blockIdx.x / groups_per_row;
+  const int64_t j = blockIdx.x - row * groups_per_row;
+  const int64_t xb = row * ld_x + j * g;
+  const int64_t qb = row * K + j * g;
+  float f[NV][8];
+  float a = 0.0f;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int64_t i = ((int64_t)v * kThreads + threadIdx.x) * 8;
+    if (i < g) {
+      load8<XT>(x, xb + i, f[v]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) a = fmaxf(a, fabsf(f[v][t]));
+    }
+  }
+  a = block_max(a, red);
+  const float sc = group_scale<UE>(a, eps, qmax);
+  if (threadIdx.x == 0) s[blockIdx.x] = sc;
+  const Divider<UE> div(sc);
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int64_t i = ((int64_t)v * kThreads + threadIdx.x) * 8;
+    if (i < g) {
+      float y[8];
+      div.apply8(f[v], y, qmin, qmax);
+      *reinterpret_cast<uint2*>(q + qb + i) = encode8<FP8>(y);
+    }
+  }
+}
+
 template <int XT, bool VEC>
 __global__ __launch_bounds__(kThreads) void amax_partials(const void* __restrict__ x, int64_t M,
                                                          int64_t K, int64_t ld_x,
@@ -386,6 +428,19 @@ hipError_t dispatch(const QuantArgs& a, hipStream_t st) {
     const int64_t ngroups = a.M * (a.K / g);
     if (ngroups > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)ngroups);
+    if (vec && g % 8 == 0 && g <= kThreads * 8 * 4) {
+      const int nv = (int)((g + kThreads * 8 - 1) / (kThreads * 8));
+      if (nv == 1)
+        hipLaunchKernelGGL((quant_group_regs<XT, FP8, UE, 1>), grid, blk, 0, st, a.x, a.K, a.ld_x,
+                           q, a.s, g, a.eps, a.qmin, a.qmax);
+      else if (nv == 2)
+        hipLaunchKernelGGL((quant_group_regs<XT, FP8, UE, 2>), grid, blk, 0, st, a.x, a.K, a.ld_x,
+                           q, a.s, g, a.eps, a.qmin, a.qmax);
+      else
+        hipLaunchKernelGGL((quant_group_regs<XT, FP8, UE, 4>), grid, blk, 0, st, a.x, a.K, a.ld_x,
+                           q, a.s, g, a.eps, a.qmin, a.qmax);
+      return hipGetLastError();
+    }
     if (vec && g % 8 == 0)
       hipLaunchKernelGGL((quant_group_block<XT, FP8, UE, true>), grid, blk, 0, st, a.x, a.K,
                          a.ld_x, q, a.s, g, a.eps, a.qmin, a.qmax);

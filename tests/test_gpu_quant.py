@@ -138,6 +138,15 @@ def test_int8_per_token_small_and_groups():
     check(synth.activations(7, 2048, "bf16", seed=4), 128, int8=True)
 
 
+@pytest.mark.parametrize("K", [2056, 4104, 16384])
+def test_per_token_rows_around_register_limit(K):
+    """Rows of up to 8192 elements stay in registers (one, two or four
+    8-element vectors per thread); longer rows take the two-pass kernel."""
+    x = synth.activations(3, K, "bf16", seed=K)
+    check(x, K, int8=True)
+    check(x, K)
+
+
 @pytest.mark.parametrize("int8", [False, True])
 def test_per_tensor_dynamic(int8):
     m = q8()
