@@ -170,19 +170,48 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
   int64_t m_lo, m_hi, n0;
   int e = 0;
   if constexpr (GROUPED) {
-    int64_t total = 0;
-    for (int x = 0; x < p.E; ++x) {
-      const int64_t mt = (p.offsets[x + 1] - p.offsets[x] + BM - 1) / BM;
-      total += mt * p.tiles_n;
+    // (expert, m tile, n tile) of this workgroup from the experts' row
+    // offsets, 64 experts at a time across the lanes of every wave (a serial
+    // walk over the experts would cost one dependent load per expert): a
+    // reduction gives the number of tiles, an inclusive scan and a ballot
+    // find the expert whose tiles contain this one. The host keeps the tile
+    // count below 2^31.
+    auto tiles_of = [&](int x) -> int {
+      if (x >= p.E) return 0;
+      return ((p.offsets[x + 1] - p.offsets[x] + BM - 1) / BM) * (int)p.tiles_n;
+    };
+    int total = 0;
+    for (int c = 0; c < p.E; c += 64) {
+      int t = tiles_of(c + lane);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, 64);
+      total += t;
     }
-    if ((int64_t)blockIdx.x >= total) return;
-    int64_t L = xcd_remap(blockIdx.x, total);
-    int64_t mt = 0;
-    for (e = 0; e < p.E; ++e) {
-      mt = (p.offsets[e + 1] - p.offsets[e] + BM - 1) / BM;
-      if (L < mt * p.tiles_n) break;
-      L -= mt * p.tiles_n;
+    total = __builtin_amdgcn_readfirstlane(total);
+    if ((int)blockIdx.x >= total) return;
+    int L = (int)xcd_remap(blockIdx.x, total);
+    int base = 0, mt = 1;
+    for (int c = 0; c < p.E; c += 64) {
+      const int t = tiles_of(c + lane);
+      int incl = t;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      const int chunk = __shfl(incl, 63, 64);
+      if (L < base + chunk) {
+        const int le = __builtin_ctzll(__ballot(base + incl > L));
+        e = c + le;
+        L -= base + __shfl(incl - t, le, 64);
+        mt = __shfl(t, le, 64) / (int)p.tiles_n;
+        break;
+      }
+      base += chunk;
     }
+    e = __builtin_amdgcn_readfirstlane(e);
+    L = __builtin_amdgcn_readfirstlane(L);
+    mt = __builtin_amdgcn_readfirstlane(mt);
     const int64_t tn = L / mt, tm = L - tn * mt;
     m_lo = p.offsets[e] + tm * BM;
     m_hi = m_lo + BM < p.offsets[e + 1] ? m_lo + BM : p.offsets[e + 1];
