@@ -69,11 +69,24 @@ class KernelTimer:
                 "p10": sorted(v)[len(v) // 10], "p90": sorted(v)[(len(v) * 9) // 10], "n": len(v)}
 
 
-def source_sha(*names: str) -> str:
+def tile_kernel_sha():
+    """Hash of the sources the prefill tile kernel is built from: its
+    parameter block, device helpers and kernel, its host launch code, and the
+    shared headers. Other kernels in the same file do not change it."""
+    csrc = os.path.join(ROOT, "int8_quantized_gemm_amd", "csrc")
+    try:
+        with open(os.path.join(csrc, "gemm_block.hip")) as f:
+            src = f.read()
+        parts = [src[src.index("struct TileParams {"):src.index("// Skinny (decode) kernel")],
+                 src[src.index("constexpr int kBM = 256"):src.index("__global__ void invert_permutation")]]
+        for n in ("tile_common.h", "q8_device.h"):
+            with open(os.path.join(csrc, n)) as f:
+                parts.append(f.read())
+    except (OSError, ValueError):
+        return None
     h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "int8_quantized_gemm_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+    for part in parts:
+        h.update(part.encode())
     return h.hexdigest()[:16]
 
 
@@ -376,7 +389,7 @@ def main() -> int:
     log(f"prefill: {pre['ms_per_step']:.3f} ms/step, GEMM {pre['gemm_us']['mean']:.1f} us "
         f"= {pre['gemm_tflops']:.0f} TFLOP/s")
     M, N, K, blk = pre["shape"]
-    sha = source_sha("gemm_block.hip", "tile_common.h", "q8_device.h")
+    sha = tile_kernel_sha()
     roof = {"bound": "mfma", "achieved": round(pre["gemm_tflops"], 1), "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s", "frac": round(pre["gemm_tflops"] / PEAK_FP8_TFLOPS, 4),
             "traffic": measured_traffic("gemm_tile", "prefill_4096x7168x7168", sha),
