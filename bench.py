@@ -262,6 +262,34 @@ def bench_int8(torch, q8, synth, reps):
             "TOP/s": round(tops, 1), "frac_int8_peak": round(tops / PEAK_INT8_TOPS, 4)}
 
 
+def bench_fp8_scaled(torch, q8, synth, reps):
+    """Per-token FP8 quant of the prefill activation + FP8 GEMM against
+    per-channel FP8 weights (one scale per row), bf16 out."""
+    M, N, K = 4096, 7168, 7168
+    dev = "cuda:0"
+    x = synth.activations(M, K, "bf16", seed=0).to(dev)
+    Wq, Ws = synth.fp8_block_weights(N, K, 1, K, seed=0)
+    Wq, Ws = Wq.to(dev).view(torch.float8_e4m3fn), Ws.reshape(-1).to(dev)
+    aq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+    sa = torch.empty((M, 1), dtype=torch.float32, device=dev)
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    gt, qt = KernelTimer(torch), KernelTimer(torch)
+    for i in range(reps + 5):
+        if i >= 5:
+            with qt:
+                q8.quant_8bit(x, aq, sa, K, EPS, -448.0, 448.0, False)
+            with gt:
+                q8.scaled_mm_fp8(aq, Wq, sa.reshape(-1), Ws, torch.bfloat16, out=D)
+        else:
+            q8.quant_8bit(x, aq, sa, K, EPS, -448.0, 448.0, False)
+            q8.scaled_mm_fp8(aq, Wq, sa.reshape(-1), Ws, torch.bfloat16, out=D)
+    torch.cuda.synchronize()
+    g = gt.us()
+    tf = 2.0 * M * N * K / (g["median"] * 1e-6) / 1e12
+    return {"gemm_us": round(g["median"], 2), "quant_us": round(qt.us()["median"], 2),
+            "TFLOP/s": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+
+
 def bench_moe(torch, q8, synth, reps):
     T, E, topk, N, K, blk = 4096, 64, 8, 2048, 7168, 128
     dev = "cuda:0"
@@ -404,6 +432,8 @@ def main() -> int:
         log(f"quant: {json.dumps(paths['quant_4096x7168'])}")
         paths["int8_2048x8192x8192"] = bench_int8(torch, q8, synth, reps)
         log(f"int8: {json.dumps(paths['int8_2048x8192x8192'])}")
+        paths["fp8_per_token_x_channel_4096x7168x7168"] = bench_fp8_scaled(torch, q8, synth, reps)
+        log(f"fp8 scaled: {json.dumps(paths['fp8_per_token_x_channel_4096x7168x7168'])}")
         paths["moe_4096tok_e64_top8"] = bench_moe(torch, q8, synth, reps)
         log(f"moe: {json.dumps(paths['moe_4096tok_e64_top8'])}")
     cpu = cpu_baseline(pre, args.cpu_rows) if args.cpu_rows > 0 else None

@@ -145,6 +145,28 @@ int scaled_mm_int8(const int8_t* A, const float* sa, int64_t sa_numel,
                    int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
+ * FP8 e4m3fn scaled GEMM with per-tensor or per-row / per-column scales.
+ * "Implementation: Sgl project Sglang GEMM Interface", Description > Scaled
+ * Matrix Multiplication (fp8_scaled_mm: per-tensor scales, optional bias,
+ * output dtype) and its usage example (scales of shape (1,) or per row of A /
+ * per column of B); vLLM scaled_mm page, the per-tensor x per-tensor and
+ * per-token x per-channel rule, broadcast here to all four combinations.
+ *
+ * A [M, K] e4m3fn, W [N, K] e4m3fn (row-major, K contiguous; the pages' (K, N)
+ * mat_b is the transposed view of this W). acc[m,n] = sum_k A[m,k] * W[n,k]
+ * accumulated in float32 inside the matrix cores (order unspecified).
+ * D = ((acc * sa[m or 0]) * sb[n or 0]) (+ (float)bias[n]) in float32 without
+ * contraction, then RNE to out_dtype (Q8_BF16 or Q8_F16); bias [N] of the
+ * output dtype or NULL. sa_numel in {1, M}, sb_numel in {1, N}.
+ * Rules: N % 16 == 0, K % 16 == 0, A and W each below 4 GiB. Caller owns all
+ * buffers; asynchronous on stream; errors as for scaled_mm_int8.
+ */
+int scaled_mm_fp8(const void* A, const float* sa, int64_t sa_numel,
+                  const void* W, const float* sb, int64_t sb_numel,
+                  const void* bias, void* D, q8_dtype out_dtype,
+                  int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
  * MoE routing tables from the router's top-k expert ids.
  * "Implementation: Sgl project Sglang CUTLASS MoE", Description and I/O
  * Contract (get_cutlass_w4a8_moe_mm_data): expert offsets, per-expert problem

@@ -41,6 +41,7 @@ EXPORTS = (
     "quant_8bit_workspace_size", "quant_8bit",
     "blockwise_scaled_mm_workspace_size", "blockwise_scaled_mm",
     "scaled_mm_int8",
+    "scaled_mm_fp8",
     "moe_mm_data_workspace_size", "moe_mm_data",
     "grouped_blockwise_scaled_mm_workspace_size", "grouped_blockwise_scaled_mm",
     "shuffle_rows",
@@ -64,6 +65,7 @@ _bmm_ws = _sig("blockwise_scaled_mm_workspace_size", _sz, _i64, _i64, _i64, _i, 
 _bmm = _sig("blockwise_scaled_mm", _i, _p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i, _i, _p,
             _sz, _p)
 _imm = _sig("scaled_mm_int8", _i, _p, _p, _i64, _p, _p, _i64, _p, _p, _i, _i64, _i64, _i64, _p)
+_fmm = _sig("scaled_mm_fp8", _i, _p, _p, _i64, _p, _p, _i64, _p, _p, _i, _i64, _i64, _i64, _p)
 _moe_ws = _sig("moe_mm_data_workspace_size", _sz, _i64, _i, _i)
 _moe = _sig("moe_mm_data", _i, _p, _i64, _i, _i, _i64, _i64, _p, _p, _p, _p, _p, _p, _sz, _p)
 _gmm_ws = _sig("grouped_blockwise_scaled_mm_workspace_size", _sz, _i, _i64, _i64, _i64, _i, _i)
@@ -213,6 +215,29 @@ def scaled_mm_int8(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torch.Ten
     _check(_imm(_ptr(mat_a), _ptr(scales_a), 0 if scales_a is None else scales_a.numel(),
                 _ptr(mat_b), _ptr(scales_b), 0 if scales_b is None else scales_b.numel(),
                 _ptr(bias), _ptr(out), _dt(out.dtype), M, N, K, _stream(dev)))
+    return out
+
+
+def scaled_mm_fp8(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torch.Tensor,
+                  scales_b: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                  bias: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """FP8 per-tensor / per-token x per-channel: ``mat_a`` [M, K] e4m3fn;
+    ``mat_b`` [N, K] e4m3fn (or its ``.t()`` view [K, N]); ``scales_a`` numel 1
+    or M, ``scales_b`` numel 1 or N (float32)."""
+    dev = _dev(mat_a, mat_b, scales_a, scales_b, bias, out)
+    _contig(mat_a, scales_a, scales_b, bias)
+    M, K = mat_a.shape
+    if mat_b.is_contiguous() and mat_b.shape[1] == K:
+        N = mat_b.shape[0]
+    elif mat_b.shape[0] == K and mat_b.stride() == (1, K):
+        N = mat_b.shape[1]  # transposed view of a contiguous [N, K]
+    else:
+        raise ValueError("mat_b must be [N, K] contiguous or the .t() view of one")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    _contig(out)
+    _check(_fmm(_ptr(mat_a), _ptr(scales_a), scales_a.numel(), _ptr(mat_b), _ptr(scales_b),
+                scales_b.numel(), _ptr(bias), _ptr(out), _dt(out.dtype), M, N, K, _stream(dev)))
     return out
 
 

@@ -1,6 +1,6 @@
 """Build libq8gemm.so (gfx950) in-tree with hipcc.
 
-Usage: ``python -m int8_quantized_gemm_amd.build`` (or ``build()`` from
+Usage: ``python int8_quantized_gemm_amd/build.py`` (or ``build()`` from
 Python). Every call recompiles every source; objects go to ``_build/`` at the
 repository root and the shared library next to this file.
 """
@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libq8gemm.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["capi.cpp", "quant.hip", "gemm_block.hip", "gemm_int8.hip", "moe.hip"]
+SOURCES = ["capi.cpp", "quant.hip", "gemm_block.hip", "gemm_scaled.hip", "moe.hip"]
 ARCH = "gfx950"
 
 

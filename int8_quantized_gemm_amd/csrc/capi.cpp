@@ -148,8 +148,31 @@ int scaled_mm_int8(const int8_t* A, const float* sa, int64_t sa_numel, const int
   }
   if (M == 0) return ok();
   if (!A || !W || !D) return fail(Q8_EINVAL, "%s: null pointer", fn);
-  q8::Int8GemmArgs a{A, sa, sa_numel, W, sb, sb_numel, bias, D, out_dtype, M, N, K};
-  return hip_status(q8::launch_int8(a, stream), fn);
+  q8::ScaledGemmArgs a{A, sa, sa_numel, W, sb, sb_numel, bias, D, out_dtype, M, N, K, false};
+  return hip_status(q8::launch_scaled(a, stream), fn);
+}
+
+int scaled_mm_fp8(const void* A, const float* sa, int64_t sa_numel, const void* W,
+                  const float* sb, int64_t sb_numel, const void* bias, void* D,
+                  q8_dtype out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  static const char* fn = "scaled_mm_fp8";
+  if (out_dtype != Q8_BF16 && out_dtype != Q8_F16)
+    return fail(Q8_EINVAL, "%s: out_dtype must be BF16 or F16", fn);
+  if (M < 0 || N < 1 || K < 1) return fail(Q8_ESHAPE, "%s: need M >= 0, N >= 1, K >= 1", fn);
+  if (N % 16 != 0 || K % 16 != 0)
+    return fail(Q8_ESHAPE, "%s: N (%lld) and K (%lld) must be multiples of 16", fn, (long long)N,
+                (long long)K);
+  if (M * K >= kFourGiB || N * K >= kFourGiB)
+    return fail(Q8_EUNSUPPORTED, "%s: an operand (A or W) reaches 4 GiB", fn);
+  if (!sa || !sb) return fail(Q8_EINVAL, "%s: null scale pointer", fn);
+  if (!(sa_numel == 1 || sa_numel == M))
+    return fail(Q8_EUNSUPPORTED, "%s: scales_a numel %lld is neither 1 nor M", fn, (long long)sa_numel);
+  if (!(sb_numel == 1 || sb_numel == N))
+    return fail(Q8_EUNSUPPORTED, "%s: scales_b numel %lld is neither 1 nor N", fn, (long long)sb_numel);
+  if (M == 0) return ok();
+  if (!A || !W || !D) return fail(Q8_EINVAL, "%s: null pointer", fn);
+  q8::ScaledGemmArgs a{A, sa, sa_numel, W, sb, sb_numel, bias, D, out_dtype, M, N, K, true};
+  return hip_status(q8::launch_scaled(a, stream), fn);
 }
 
 size_t moe_mm_data_workspace_size(int64_t T, int topk, int E) {

@@ -1,38 +1,72 @@
-// INT8 W8A8 scaled GEMM for gfx950.
+// Per-tensor / per-token x per-channel scaled GEMMs for gfx950: INT8 W8A8
+// and FP8 e4m3fn.
 //
 // vLLM scaled_mm page, AiterInt8ScaledMMLinearKernel.apply_weights: output =
 // mm(scale_a * a, scale_b * b) with numpy broadcasting, a [M, K], weights
 // [N, K]; per-tensor x per-tensor and per-token x per-channel scales (the
-// other two combinations broadcast the same way here).
+// other two combinations broadcast the same way here). "Implementation: Sgl
+// project Sglang GEMM Interface", Scaled Matrix Multiplication: int8_scaled_mm
+// and fp8_scaled_mm (per-tensor or per-row / per-column scales, optional
+// bias, output dtype).
 //
-// The int32 accumulator is exact, so the whole K loop accumulates inside the
-// matrix cores (v_mfma_i32_16x16x64_i8, chained), with no per-block work; the
-// scales and bias are applied once in the epilogue in float32 without FMA
+// With one scale per row and per column the whole K loop accumulates inside
+// the matrix cores (INT8: v_mfma_i32_16x16x64_i8, exact int32; FP8:
+// v_mfma_f32_16x16x128_f8f6f4, float32), with no per-block work; the scales
+// and bias are applied once in the epilogue in float32 without FMA
 // contraction: ((float)acc * sa) * sb + bias, then round to nearest even.
-// gemm_int8_pipe (K % 128 == 0) uses the FP8 tile kernel's pipeline;
-// gemm_int8_tile (register-staged loads, zero-filled partial last slab) covers
-// K % 128 != 0.
+// gemm_scaled_pipe (K % 128 == 0) uses the block-FP8 tile kernel's pipeline;
+// gemm_scaled_tile (register-staged loads, zero-filled partial last slab)
+// covers K % 128 != 0.
 #include "q8_internal.h"
 #include "tile_common.h"
 
 namespace q8 {
 namespace {
 
-struct Int8Params {
-  const int8_t* A;
+struct ScaledParams {
+  const uint8_t* A;
   const float* sa;
-  const int8_t* W;
+  const uint8_t* W;
   const float* sb;
   const void* bias;
   void* D;
   int64_t M, N, K;
   int sa_per_row, sb_per_col;
-  int out_kind;  // 0 = int32, 1 = bf16, 2 = f16
+  int out_kind;  // 0 = int32 (INT8 only), 1 = bf16, 2 = f16
   int64_t tiles_m, tiles_n;
 };
 
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_int8_tile(Int8Params p) {
+// Accumulator and MFMA per operand type. A 128-byte K slab is two
+// 16x16x64 INT8 MFMAs or one 16x16x128 FP8 MFMA; lane group g supplies
+// chunks g and g + 4 of the slab for both operands.
+template <bool FP8>
+struct Mma;
+template <>
+struct Mma<false> {
+  typedef i32x4 acc_t;
+  static __device__ __forceinline__ acc_t zero() { return i32x4{0, 0, 0, 0}; }
+  static __device__ __forceinline__ acc_t slab(const i32x4& a0, const i32x4& a1, const i32x4& b0,
+                                               const i32x4& b1, acc_t c) {
+    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, c, 0, 0, 0);
+  }
+};
+template <>
+struct Mma<true> {
+  typedef f32x4 acc_t;
+  static __device__ __forceinline__ acc_t zero() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+  static __device__ __forceinline__ acc_t slab(const i32x4& a0, const i32x4& a1, const i32x4& b0,
+                                               const i32x4& b1, acc_t c) {
+    const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    const i32x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    // cbsz = blgp = 0 (both e4m3), zero scale operands: the unscaled MFMA
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
+};
+
+template <int BM, int BN, int WM, int WN, bool FP8>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_scaled_tile(ScaledParams p) {
+  typedef typename Mma<FP8>::acc_t acc_t;
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
@@ -52,8 +86,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_int8_tile(Int8Params p) 
   grouped_order(t, p.tiles_m, p.tiles_n, 8, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
 
-  const int8_t* a_src[A_CH];
-  const int8_t* b_src[B_CH];
+  const uint8_t* a_src[A_CH];
+  const uint8_t* b_src[B_CH];
 #pragma unroll
   for (int c = 0; c < A_CH; ++c) {
     const int idx = tid + c * NT, r = idx >> 3, ch = idx & 7;
@@ -95,11 +129,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_int8_tile(Int8Params p) 
     }
   };
 
-  i32x4 acc[FM][FN];
+  acc_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+    for (int j = 0; j < FN; ++j) acc[i][j] = Mma<FP8>::zero();
 
   const int KT = (int)((K + 127) / 128);
   gload(0);
@@ -108,19 +142,18 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_int8_tile(Int8Params p) 
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < KT) gload((int64_t)(kt + 1) * 128);
+    i32x4 bf[2][FN];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      i32x4 bf[FN];
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bf[j] = *reinterpret_cast<const i32x4*>(&sB[buf][swz(wn * TN + j * 16 + r16, 4 * h + g)]);
+        bf[h][j] = *reinterpret_cast<const i32x4*>(&sB[buf][swz(wn * TN + j * 16 + r16, 4 * h + g)]);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const i32x4 af = *reinterpret_cast<const i32x4*>(&sA[buf][swz(wm * TM + i * 16 + r16, 4 * h + g)]);
+    for (int i = 0; i < FM; ++i) {
+      const i32x4 af0 = *reinterpret_cast<const i32x4*>(&sA[buf][swz(wm * TM + i * 16 + r16, g)]);
+      const i32x4 af1 = *reinterpret_cast<const i32x4*>(&sA[buf][swz(wm * TM + i * 16 + r16, 4 + g)]);
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[j], acc[i][j], 0, 0, 0);
-      }
+      for (int j = 0; j < FN; ++j) acc[i][j] = Mma<FP8>::slab(af0, af1, bf[0][j], bf[1][j], acc[i][j]);
     }
     if (kt + 1 < KT) lstore(buf ^ 1);
     __syncthreads();
@@ -144,9 +177,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_int8_tile(Int8Params p) 
       for (int rr = 0; rr < 4; ++rr) {
         const int64_t row = m0 + wm * TM + i * 16 + 4 * g + rr;
         if (row >= M) continue;
-        const int v = acc[i][j][rr];
-        if (p.out_kind == 0) {
-          static_cast<int32_t*>(p.D)[row * N + col] = v;
+        const auto v = acc[i][j][rr];
+        if (!FP8 && p.out_kind == 0) {
+          static_cast<int32_t*>(p.D)[row * N + col] = (int32_t)v;
         } else {
           const float sav = p.sa[p.sa_per_row ? row : 0];
           float o = __fmul_rn(__fmul_rn((float)v, sav), sbv);
@@ -164,8 +197,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_int8_tile(Int8Params p) 
 // conflict-free fragment layout) with the int32 accumulation kept inside the
 // matrix cores. MFMA operand 0 is the weight fragment, so a lane's four
 // accumulators are four consecutive output columns of one row.
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_int8_pipe(Int8Params p) {
+template <int BM, int BN, int WM, int WN, bool FP8>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_scaled_pipe(ScaledParams p) {
+  typedef typename Mma<FP8>::acc_t acc_t;
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
@@ -211,11 +245,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_int8_pipe(Int8Params p) {
     }
   };
 
-  i32x4 acc[FM][FN];
+  acc_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+    for (int j = 0; j < FN; ++j) acc[i][j] = Mma<FP8>::zero();
 
   // lane group g holds 16-byte chunks g (first 64-wide K step) and g + 4
   // (second) of each row: the same K assignment for both operands
@@ -238,10 +272,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_int8_pipe(Int8Params p) {
         av[(i + 1) & 1][1] = *reinterpret_cast<const i32x4*>(la + swz(row, g + 4));
       }
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bw[h][j], av[i & 1][h], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = Mma<FP8>::slab(bw[0][j], bw[1][j], av[i & 1][0], av[i & 1][1], acc[i][j]);
     }
   };
   auto step = [&](int kt, bool refill, uint8_t* __restrict__ na, uint8_t* __restrict__ nb,
@@ -268,9 +300,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_int8_pipe(Int8Params p) {
     for (int j = 0; j < FN; ++j) {
       const int64_t n = n0 + wn * TN + j * 16 + 4 * g;
       if (n >= N) continue;  // N % 16 == 0: n .. n+3 all in range otherwise
-      const i32x4 v = acc[i][j];
-      if (p.out_kind == 0) {
-        *reinterpret_cast<i32x4*>(static_cast<int32_t*>(p.D) + m * N + n) = v;
+      const acc_t v = acc[i][j];
+      if (!FP8 && p.out_kind == 0) {
+        *reinterpret_cast<acc_t*>(static_cast<int32_t*>(p.D) + m * N + n) = v;
       } else {
         uint32_t o[4];
 #pragma unroll
@@ -294,10 +326,12 @@ constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 4;
 
 }  // namespace
 
-hipError_t launch_int8(const Int8GemmArgs& a, hipStream_t st) {
+hipError_t launch_scaled(const ScaledGemmArgs& a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
-  Int8Params p{};
-  p.A = a.A; p.sa = a.sa; p.W = a.W; p.sb = a.sb; p.bias = a.bias; p.D = a.D;
+  ScaledParams p{};
+  p.A = static_cast<const uint8_t*>(a.A); p.sa = a.sa;
+  p.W = static_cast<const uint8_t*>(a.W); p.sb = a.sb;
+  p.bias = a.bias; p.D = a.D;
   p.M = a.M; p.N = a.N; p.K = a.K;
   p.sa_per_row = a.sa_numel > 1 || (a.sa_numel == a.M && a.M == 1);
   p.sb_per_col = a.sb_numel > 1 || (a.sb_numel == a.N && a.N == 1);
@@ -309,12 +343,14 @@ hipError_t launch_int8(const Int8GemmArgs& a, hipStream_t st) {
   // the pipelined kernel needs whole 128-byte K slabs and 16-byte aligned rows
   // of D (N % 16 == 0 always holds here)
   const bool pipe = a.K % 128 == 0 && (uintptr_t)a.D % 16 == 0 && (uintptr_t)a.bias % 8 == 0;
-  if (pipe)
-    hipLaunchKernelGGL((gemm_int8_pipe<kBM, kBN, kWM, kWN>), dim3((unsigned)tiles),
-                       dim3(kWM * kWN * 64), 0, st, p);
-  else
-    hipLaunchKernelGGL((gemm_int8_tile<kBM, kBN, kWM, kWN>), dim3((unsigned)tiles),
-                       dim3(kWM * kWN * 64), 0, st, p);
+  const dim3 grid((unsigned)tiles), block(kWM * kWN * 64);
+  if (a.fp8) {
+    if (pipe) hipLaunchKernelGGL((gemm_scaled_pipe<kBM, kBN, kWM, kWN, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((gemm_scaled_tile<kBM, kBN, kWM, kWN, true>), grid, block, 0, st, p);
+  } else {
+    if (pipe) hipLaunchKernelGGL((gemm_scaled_pipe<kBM, kBN, kWM, kWN, false>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((gemm_scaled_tile<kBM, kBN, kWM, kWN, false>), grid, block, 0, st, p);
+  }
   return hipGetLastError();
 }
 

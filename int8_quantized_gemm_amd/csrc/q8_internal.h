@@ -38,13 +38,14 @@ hipError_t launch_grouped(const BlockGemmArgs& a, int64_t total_m, int32_t* c_in
                           const int32_t* c_map, hipStream_t stream);
 
 // ---- INT8 GEMM ----------------------------------------------------------------
-struct Int8GemmArgs {
-  const int8_t* A; const float* sa; int64_t sa_numel;
-  const int8_t* W; const float* sb; int64_t sb_numel;
+struct ScaledGemmArgs {
+  const void* A; const float* sa; int64_t sa_numel;
+  const void* W; const float* sb; int64_t sb_numel;
   const void* bias; void* D; q8_dtype out_dtype;
   int64_t M, N, K;
+  bool fp8;  // e4m3fn operands (else int8)
 };
-hipError_t launch_int8(const Int8GemmArgs& a, hipStream_t stream);
+hipError_t launch_scaled(const ScaledGemmArgs& a, hipStream_t stream);
 
 // ---- MoE routing + row gather -------------------------------------------------
 size_t moe_workspace_ints(int64_t T, int topk, int E);

@@ -20,6 +20,12 @@ apply_weights: ``out = mm(scale_a * a, scale_b * b)`` with numpy broadcasting,
 weights ``[N, K]``; the integer accumulator ``acc = sum_k a[m, k] * w[n, k]``
 is exact (integer products below 2^14, sums below 2^27, so float64 BLAS is
 exact too), then ``acc * sa * sb + bias`` in float64.
+
+FP8 with per-tensor or per-row / per-column scales, from "Implementation: Sgl
+project Sglang GEMM Interface" (fp8_scaled_mm: scales of shape (1,) or per row
+of A / per column of B, optional bias) and the same broadcasting rule: the
+exact float64 product of the decoded codes over the whole K (the exactness
+argument above holds for up to 2^17 terms), times ``sa * sb``, plus bias.
 """
 from __future__ import annotations
 
@@ -91,6 +97,28 @@ def scaled_mm_int8(Aq, sa, Wq, sb, bias=None, acc=None) -> np.ndarray:
     sa_col = sa.reshape(-1, 1)   # [M, 1] or [1, 1]: numpy broadcasting
     sb_row = sb.reshape(1, -1)   # [1, N] or [1, 1]
     D = acc.astype(np.float64) * sa_col * sb_row
+    if bias is not None:
+        D = D + np.asarray(bias, dtype=np.float64)[None, :]
+    return D
+
+
+def scaled_mm_fp8(Aq, sa, Wq, sb, bias=None) -> np.ndarray:
+    """FP8 per-tensor / per-token x per-channel -> float64 ``D [M, N]``.
+
+    ``Aq [M, K]`` / ``Wq [N, K]`` uint8 e4m3fn codes; ``sa`` numel 1 or M,
+    ``sb`` numel 1 or N; ``bias [N]`` or None.
+    """
+    A = e4m3.decode(Aq)
+    W = e4m3.decode(Wq)
+    M, K = A.shape
+    N = W.shape[0]
+    if K > 2 ** 17:
+        raise ValueError("K above 2^17: the float64 sum is no longer exact")
+    sa = np.asarray(sa, dtype=np.float64).reshape(-1)
+    sb = np.asarray(sb, dtype=np.float64).reshape(-1)
+    if sa.size not in (1, M) or sb.size not in (1, N):
+        raise ValueError("scale numel must be 1 or the matching dimension")
+    D = (A @ W.T) * sa.reshape(-1, 1) * sb.reshape(1, -1)
     if bias is not None:
         D = D + np.asarray(bias, dtype=np.float64)[None, :]
     return D

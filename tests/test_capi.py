@@ -32,7 +32,7 @@ def q8():
 
 def test_header_declares_the_five_entry_points():
     names = declared_functions()
-    for n in ("quant_8bit", "blockwise_scaled_mm", "scaled_mm_int8", "moe_mm_data",
+    for n in ("quant_8bit", "blockwise_scaled_mm", "scaled_mm_int8", "scaled_mm_fp8", "moe_mm_data",
               "grouped_blockwise_scaled_mm", "shuffle_rows", "q8gemm_last_error"):
         assert n in names
 
@@ -108,6 +108,20 @@ def test_int8_validation(q8):
     assert q8._imm(p, 8, 1, p, p, 1, p, p, q8.Q8_I32, 4, 128, 128, p) == q8.Q8_EINVAL    # scales with I32
     assert q8._imm(p, 8, 1, p, 8, 1, p, p, q8.Q8_F32, 4, 128, 128, p) == q8.Q8_EINVAL
     assert q8._imm(p, 8, 1, p, 8, 1, p, p, q8.Q8_BF16, 0, 128, 128, p) == q8.Q8_OK
+
+
+def test_fp8_scaled_validation(q8):
+    p = None
+    assert q8._fmm(p, p, 1, p, p, 1, p, p, q8.Q8_BF16, 4, 100, 128, p) == q8.Q8_ESHAPE   # N % 16
+    assert q8._fmm(p, p, 1, p, p, 1, p, p, q8.Q8_BF16, 4, 128, 120, p) == q8.Q8_ESHAPE   # K % 16
+    assert q8._fmm(p, 8, 3, p, 8, 1, p, p, q8.Q8_BF16, 4, 128, 128, p) == q8.Q8_EUNSUPPORTED
+    assert "scales_a" in q8.last_error()
+    assert q8._fmm(p, 8, 4, p, 8, 7, p, p, q8.Q8_BF16, 4, 128, 128, p) == q8.Q8_EUNSUPPORTED
+    assert q8._fmm(p, p, 1, p, 8, 1, p, p, q8.Q8_BF16, 4, 128, 128, p) == q8.Q8_EINVAL    # null scale
+    assert q8._fmm(p, 8, 1, p, 8, 1, p, p, q8.Q8_I32, 4, 128, 128, p) == q8.Q8_EINVAL    # no raw output
+    assert q8._fmm(p, 8, 1, p, 8, 1, p, p, q8.Q8_BF16, 4, 128, 128, p) == q8.Q8_EINVAL   # null operands
+    assert q8._fmm(p, 8, 1, p, 8, 1, p, p, q8.Q8_BF16, 0, 128, 128, p) == q8.Q8_OK
+    assert q8._fmm(p, 8, 1, p, 8, 1, p, p, q8.Q8_F16, 1 << 20, 128, 4096, p) == q8.Q8_EUNSUPPORTED  # 4 GiB
 
 
 def test_moe_and_grouped_validation(q8):

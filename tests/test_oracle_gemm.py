@@ -8,7 +8,11 @@
   single library matmul (the vLLM CPU per-tensor kernel runs per-tensor FP8
   as one synthetic block);
 * block-size independence when all scales are 1;
-* INT8: Python-integer brute force and per-tensor/per-token equivalence.
+* INT8: Python-integer brute force and per-tensor/per-token equivalence;
+* FP8 per-tensor / per-token x per-channel: exact rational brute force, and
+  the special case "per-channel weight scales = blocks of one weight row"
+  of the block GEMM with one K block (and with power-of-two scales, any K
+  blocking).
 """
 from fractions import Fraction
 
@@ -175,3 +179,47 @@ def test_int8_extreme_accumulator_fits_int32():
     W = np.full((2, K), -128, np.int8)
     acc = gemm.int8_acc(A, W)
     assert np.all(acc == 128 * 128 * K)
+
+
+def test_fp8_scaled_fraction_brute_force():
+    r = np.random.default_rng(31)
+    M, N, K = 4, 6, 160
+    Aq = rand_codes(r, (M, K))
+    Wq = rand_codes(r, (N, K))
+    sa = rand_scales(r, (M,))
+    sb = rand_scales(r, (N,))
+    bias = r.standard_normal(N).astype(F32)
+    D = gemm.scaled_mm_fp8(Aq, sa, Wq, sb, bias)
+    dec = [Fraction(float(v)) if np.isfinite(v) else None for v in e4m3.DECODE]
+    for m in range(M):
+        for n in range(N):
+            acc = sum(dec[Aq[m, k]] * dec[Wq[n, k]] for k in range(K))
+            ex = acc * Fraction(float(sa[m])) * Fraction(float(sb[n])) + Fraction(float(bias[n]))
+            assert abs(Fraction(float(D[m, n])) - ex) <= abs(ex) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 60)
+
+
+def test_fp8_scaled_is_block_gemm_with_row_blocks():
+    """Per-channel weight scales are weight blocks of one row (bn = 1) and
+    per-token activation scales are one value per row for every K block:
+    with a single K block the block GEMM computes the same float64 numbers;
+    with power-of-two scales every step is exact, so any K blocking agrees."""
+    r = np.random.default_rng(32)
+    M, N, K = 7, 24, 384
+    Aq = rand_codes(r, (M, K))
+    Wq = rand_codes(r, (N, K))
+    sa = rand_scales(r, (M,))
+    sb = rand_scales(r, (N,))
+    D = gemm.scaled_mm_fp8(Aq, sa, Wq, sb)
+    Db = gemm.blockwise_scaled_mm(Aq, sa[:, None], Wq, sb[:, None], 1, K)
+    assert np.allclose(D, Db, rtol=1e-14, atol=0)
+    sa2 = np.exp2(r.integers(-8, 4, size=M)).astype(F32)
+    sb2 = np.exp2(r.integers(-8, 4, size=N)).astype(F32)
+    D2 = gemm.scaled_mm_fp8(Aq, sa2, Wq, sb2)
+    Db2 = gemm.blockwise_scaled_mm(Aq, np.tile(sa2[:, None], (1, 3)), Wq, np.tile(sb2[:, None], (1, 3)), 1, 128)
+    assert np.array_equal(D2, Db2)
+    # per-tensor x per-tensor == per-token x per-channel with constant scales
+    d1 = gemm.scaled_mm_fp8(Aq, np.array([0.5], F32), Wq, np.array([0.25], F32))
+    d2 = gemm.scaled_mm_fp8(Aq, np.full(M, 0.5, F32), Wq, np.full(N, 0.25, F32))
+    assert np.array_equal(d1, d2)
+    with pytest.raises(ValueError):
+        gemm.scaled_mm_fp8(Aq, np.ones(M + 1, F32), Wq, sb)
