@@ -305,7 +305,11 @@ def bench_moe(torch, q8, synth, reps):
     aq = torch.empty((T, K), dtype=torch.float8_e4m3fn, device=dev)
     As = torch.empty((T, K // blk), dtype=torch.float32, device=dev)
     D = torch.empty((T * topk, N), dtype=torch.bfloat16, device=dev)
+    Ds = torch.empty((T * topk, N), dtype=torch.bfloat16, device=dev)
+    gw = synth.topk_weights(T, topk, seed=0).to(dev)
+    out = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
     rt, qt, gt = KernelTimer(torch), KernelTimer(torch), KernelTimer(torch)
+    st, ft = KernelTimer(torch), KernelTimer(torch)
     for i in range(reps + 3):
         timed = i >= 3
         with (rt if timed else _Null()):
@@ -314,8 +318,16 @@ def bench_moe(torch, q8, synth, reps):
             q8.quant_8bit(x, aq, As, blk, EPS, -448.0, 448.0, False)
         with (gt if timed else _Null()):
             q8.grouped_blockwise_scaled_mm(D, aq, W, As, Ws, off, ps1, a_map=ip, c_map=op)
+        # the variant that finalizes: expert-sorted rows (no scatter), then the
+        # weighted top-k sum reads them through the output permutation
+        with (st if timed else _Null()):
+            q8.grouped_blockwise_scaled_mm(Ds, aq, W, As, Ws, off, ps1, a_map=ip)
+        with (ft if timed else _Null()):
+            q8.moe_finalize(Ds, gw, topk, op, out=out)
     torch.cuda.synchronize()
     g = gt.us()
+    fin = ft.us()["median"]
+    fin_bytes = T * topk * N * 2 + T * N * 2 + T * topk * 8
     step_us = rt.us()["median"] + qt.us()["median"] + g["median"]
     flops = 2.0 * T * topk * N * K
     nbytes = E * N * K + T * K + T * topk * N * 2 + Ws.numel() * 4 + T * (K // blk) * 4
@@ -324,7 +336,10 @@ def bench_moe(torch, q8, synth, reps):
             "gemm_tflops": round(flops / (g["median"] * 1e-6) / 1e12, 1),
             "frac_fp8_peak": round(flops / (g["median"] * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
             "gemm_GB/s_fused": round(nbytes / (g["median"] * 1e-6) / 1e9, 1),
-            "step_tflops": round(flops / (step_us * 1e-6) / 1e12, 1)}
+            "step_tflops": round(flops / (step_us * 1e-6) / 1e12, 1),
+            "grouped_gemm_sorted_us": round(st.us()["median"], 2),
+            "finalize_us": round(fin, 2), "finalize_GB/s": round(fin_bytes / (fin * 1e-6) / 1e9, 1),
+            "finalize_frac_hbm": round(fin_bytes / (fin * 1e-6) / 1e9 / 8000.0, 4)}
 
 
 class _Null:

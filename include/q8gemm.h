@@ -223,6 +223,29 @@ int grouped_blockwise_scaled_mm(const void* A, const float* As, const void* W, c
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * MoE finalize: weight every routed row by its top-k gate weight and sum each
+ * token's top-k rows.
+ * "Implementation: Sgl project Sglang Fused MoE Marlin", I/O Contract:
+ * topk_weights ("Top-k routing weights from MoE gate"), mul_topk_weights
+ * (multiply the output by them) and the reduction of the routed outputs
+ * (use_atomic_add, use_fp32_reduce). Here the reduction is deterministic.
+ *
+ * D [T*topk, N] (dtype Q8_BF16 or Q8_F16), out [T, N] of the same dtype,
+ * topk_weights [T, topk] float32 or NULL (every weight 1: a plain sum).
+ * output_permutation NULL: row (t, j) of D is t*topk + j (un-permuted GEMM
+ * output); otherwise D is in expert-sorted order and row (t, j) is
+ * output_permutation[t*topk + j] (the table moe_mm_data builds), which fuses
+ * the un-permute into this pass.
+ * out[t, n] = RNE( sum_{j < topk} w[t, j] * (float)D[row(t, j), n] ), summed
+ * in float32 in ascending j with one fused multiply-add per term.
+ * Rules: T*topk < 2^31. Rows named by output_permutation must be in D
+ * (documented, not checked). Caller owns all buffers; asynchronous on stream.
+ */
+int moe_finalize(const void* D, q8_dtype dtype, const float* topk_weights,
+                 const int32_t* output_permutation, int64_t T, int topk, int64_t N,
+                 void* out, hipStream_t stream);
+
+/*
  * Row gather.
  * "Implementation: Sgl project Sglang GEMM Interface", Utility: shuffle_rows
  * (permute rows by a destination-to-source map).

@@ -42,6 +42,7 @@ EXPORTS = (
     "blockwise_scaled_mm_workspace_size", "blockwise_scaled_mm",
     "scaled_mm_int8",
     "scaled_mm_fp8",
+    "moe_finalize",
     "moe_mm_data_workspace_size", "moe_mm_data",
     "grouped_blockwise_scaled_mm_workspace_size", "grouped_blockwise_scaled_mm",
     "shuffle_rows",
@@ -65,6 +66,7 @@ _bmm_ws = _sig("blockwise_scaled_mm_workspace_size", _sz, _i64, _i64, _i64, _i, 
 _bmm = _sig("blockwise_scaled_mm", _i, _p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i, _i, _p,
             _sz, _p)
 _imm = _sig("scaled_mm_int8", _i, _p, _p, _i64, _p, _p, _i64, _p, _p, _i, _i64, _i64, _i64, _p)
+_fin = _sig("moe_finalize", _i, _p, _i, _p, _p, _i64, _i, _i64, _p, _p)
 _fmm = _sig("scaled_mm_fp8", _i, _p, _p, _i64, _p, _p, _i64, _p, _p, _i, _i64, _i64, _i64, _p)
 _moe_ws = _sig("moe_mm_data_workspace_size", _sz, _i64, _i, _i)
 _moe = _sig("moe_mm_data", _i, _p, _i64, _i, _i, _i64, _i64, _p, _p, _p, _p, _p, _p, _sz, _p)
@@ -263,6 +265,33 @@ def moe_mm_data(topk_ids: torch.Tensor, expert_offsets: torch.Tensor,
     _check(_moe(_ptr(topk_ids), T, topk, num_experts, n, k, _ptr(expert_offsets),
                 _ptr(problem_sizes1), _ptr(problem_sizes2), _ptr(input_permutation),
                 _ptr(output_permutation), ws, wsb, _stream(dev)))
+
+
+def moe_finalize(d: torch.Tensor, topk_weights: torch.Tensor | None, topk: int,
+                 output_permutation: torch.Tensor | None = None,
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """``out[t] = sum_j topk_weights[t, j] * d[row(t, j)]`` -> ``[T, N]``.
+
+    ``d`` [T*topk, N] bf16/f16, un-permuted, or expert-sorted with
+    ``output_permutation`` (int32 [T*topk]) naming the row of each choice.
+    """
+    dev = _dev(d, topk_weights, output_permutation, out)
+    _contig(d, topk_weights, output_permutation)
+    rows, N = d.shape
+    if rows % topk:
+        raise ValueError("d must have T * topk rows")
+    T = rows // topk
+    if topk_weights is not None and (topk_weights.dtype != torch.float32 or topk_weights.numel() != rows):
+        raise ValueError("topk_weights must be float32 [T, topk]")
+    if output_permutation is not None and (output_permutation.dtype != torch.int32
+                                           or output_permutation.numel() != rows):
+        raise ValueError("output_permutation must be int32 [T * topk]")
+    if out is None:
+        out = torch.empty((T, N), dtype=d.dtype, device=dev)
+    _contig(out)
+    _check(_fin(_ptr(d), _dt(d.dtype), _ptr(topk_weights), _ptr(output_permutation), T, topk, N,
+                _ptr(out), _stream(dev)))
+    return out
 
 
 def grouped_blockwise_scaled_mm(d: torch.Tensor, a: torch.Tensor, b: torch.Tensor,

@@ -238,6 +238,19 @@ int grouped_blockwise_scaled_mm(const void* A, const float* As, const void* W, c
   return hip_status(q8::launch_grouped(a, total_m, static_cast<int32_t*>(workspace), c_map, stream), fn);
 }
 
+int moe_finalize(const void* D, q8_dtype dtype, const float* topk_weights,
+                 const int32_t* output_permutation, int64_t T, int topk, int64_t N, void* out,
+                 hipStream_t stream) {
+  static const char* fn = "moe_finalize";
+  if (dtype != Q8_BF16 && dtype != Q8_F16) return fail(Q8_EINVAL, "%s: dtype must be BF16 or F16", fn);
+  if (T < 0 || topk < 1 || N < 0) return fail(Q8_ESHAPE, "%s: need T >= 0, topk >= 1, N >= 0", fn);
+  if (T * (int64_t)topk >= kMaxI32) return fail(Q8_ESHAPE, "%s: T * topk must be below 2^31", fn);
+  if (T == 0 || N == 0) return ok();
+  if (!D || !out) return fail(Q8_EINVAL, "%s: null pointer", fn);
+  return hip_status(q8::launch_moe_finalize(D, dtype == Q8_BF16, topk_weights, output_permutation,
+                                            T, topk, N, out, stream), fn);
+}
+
 int shuffle_rows(const void* src, int64_t row_bytes, const int32_t* dst2src, int64_t dst_rows,
                  void* dst, hipStream_t stream) {
   static const char* fn = "shuffle_rows";

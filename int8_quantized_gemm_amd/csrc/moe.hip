@@ -143,6 +143,57 @@ size_t moe_workspace_ints(int64_t T, int topk, int E) {
   return (size_t)(nchunks * E);
 }
 
+// ---- finalize: weight each token's top-k expert rows and sum them ----------------
+// out[t, n] = sum_{j < topk} w[t, j] * D[row(t, j), n], in float32 in ascending
+// j with one FMA per term, then rounded to the 16-bit output type; row(t, j)
+// = perm[t * topk + j] (D in expert-sorted order) or t * topk + j. One
+// workgroup row of threads per token, eight columns (16 bytes) per thread.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(256) void moe_finalize_k(const uint16_t* __restrict__ D,
+                                                      const float* __restrict__ w,
+                                                      const int32_t* __restrict__ perm,
+                                                      int64_t T, int topk, int64_t N,
+                                                      uint16_t* __restrict__ out) {
+  constexpr int E = VEC ? 8 : 1;
+  const int64_t t = blockIdx.y;
+  const int64_t c = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * E;
+  if (c >= N) return;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  for (int j = 0; j < topk; ++j) {
+    const int64_t i = t * topk + j;
+    const int64_t row = perm ? (int64_t)perm[i] : i;
+    const float wt = w ? w[i] : 1.0f;
+    if constexpr (VEC) {
+      const uint4 v = *reinterpret_cast<const uint4*>(D + row * N + c);
+      const uint32_t h[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = BF16 ? bf16_bits_to_f32(h[q] & 0xFFFFu) : f16_bits_to_f32(h[q] & 0xFFFFu);
+        const float hi = BF16 ? bf16_bits_to_f32(h[q] >> 16) : f16_bits_to_f32(h[q] >> 16);
+        acc[2 * q] = __builtin_fmaf(wt, lo, acc[2 * q]);
+        acc[2 * q + 1] = __builtin_fmaf(wt, hi, acc[2 * q + 1]);
+      }
+    } else {
+      const uint16_t h = D[row * N + c];
+      acc[0] = __builtin_fmaf(wt, BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h), acc[0]);
+    }
+  }
+  if constexpr (VEC) {
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = BF16 ? f32_to_bf16_bits(acc[2 * q]) : f32_to_f16_bits(acc[2 * q]);
+      const uint32_t hi = BF16 ? f32_to_bf16_bits(acc[2 * q + 1]) : f32_to_f16_bits(acc[2 * q + 1]);
+      o[q] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint4*>(out + t * N + c) = uint4{o[0], o[1], o[2], o[3]};
+  } else {
+    out[t * N + c] = (uint16_t)(BF16 ? f32_to_bf16_bits(acc[0]) : f32_to_f16_bits(acc[0]));
+  }
+}
+
 hipError_t launch_moe_mm_data(const int32_t* ids, int64_t T, int topk, int E, int64_t nk,
                               int64_t kk, int32_t* offsets, int32_t* ps1, int32_t* ps2,
                               int32_t* in_perm, int32_t* out_perm, int32_t* ws,
@@ -179,6 +230,32 @@ hipError_t launch_shuffle_rows(const void* src, int64_t row_bytes, const int32_t
                        static_cast<const uint8_t*>(src), row_bytes, map, rows,
                        static_cast<uint8_t*>(dst));
   return hipGetLastError();
+}
+
+hipError_t launch_moe_finalize(const void* D, bool bf16, const float* w, const int32_t* perm,
+                               int64_t T, int topk, int64_t N, void* out, hipStream_t st) {
+  if (T == 0 || N == 0) return hipSuccess;
+  const bool vec = N % 8 == 0 && (uintptr_t)D % 16 == 0 && (uintptr_t)out % 16 == 0;
+  const int64_t per_thread = vec ? 8 : 1;
+  const int64_t bx = (N + 256 * per_thread - 1) / (256 * per_thread);
+  if (T > 65535 * 1024LL || bx > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  // grid.y is limited to 65535: tokens beyond it go in further launches
+  for (int64_t t0 = 0; t0 < T; t0 += 65535) {
+    const int64_t nt = T - t0 < 65535 ? T - t0 : 65535;
+    const dim3 grid((unsigned)bx, (unsigned)nt);
+    const uint16_t* d = static_cast<const uint16_t*>(D);
+    const float* wt = w ? w + t0 * topk : nullptr;
+    const int32_t* pm = perm ? perm + t0 * topk : nullptr;
+    uint16_t* o = static_cast<uint16_t*>(out) + t0 * N;
+#define Q8_FIN(B, V) hipLaunchKernelGGL((moe_finalize_k<B, V>), grid, dim3(256), 0, st, \
+                                        perm ? d : d + t0 * topk * N, wt, pm, nt, topk, N, o)
+    if (bf16) { if (vec) Q8_FIN(true, true); else Q8_FIN(true, false); }
+    else { if (vec) Q8_FIN(false, true); else Q8_FIN(false, false); }
+#undef Q8_FIN
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace q8

@@ -19,6 +19,11 @@ Readings taken where the page is silent:
   width ``k``;
 * ``input_permutation[p]`` is the token row feeding sorted slot ``p``;
   ``output_permutation[i]`` is the sorted slot holding flat choice ``i``.
+
+Finalize, from "Implementation: Sgl project Sglang Fused MoE Marlin", I/O
+Contract (topk_weights, mul_topk_weights, the reduction of the routed
+outputs): every routed row is multiplied by its gate weight and the top-k rows
+of each token are summed, ``out[t] = sum_j w[t, j] * D[row(t, j)]``.
 """
 from __future__ import annotations
 
@@ -70,3 +75,21 @@ def grouped_blockwise_scaled_mm(Aq, As, W, Ws, expert_offsets, input_perm,
 def unpermute(D_sorted, output_perm) -> np.ndarray:
     """``out[i] = D_sorted[output_perm[i]]``."""
     return np.asarray(D_sorted)[np.asarray(output_perm, dtype=np.int64)]
+
+
+def finalize(D, topk_weights, topk: int, output_perm=None) -> np.ndarray:
+    """``out[t] = sum_j w[t, j] * D[row(t, j)]`` in float64 -> ``[T, N]``.
+
+    ``D [T*topk, N]`` is un-permuted (row ``t*topk + j``) or, with
+    ``output_perm``, expert-sorted (row ``output_perm[t*topk + j]``).
+    ``topk_weights [T, topk]`` or None (weights 1).
+    """
+    D = np.asarray(D, dtype=np.float64)
+    rows = D.shape[0]
+    if rows % topk:
+        raise ValueError("D must have T * topk rows")
+    T = rows // topk
+    if output_perm is not None:
+        D = unpermute(D, output_perm)
+    w = np.ones((T, topk)) if topk_weights is None else np.asarray(topk_weights, np.float64).reshape(T, topk)
+    return np.einsum("tj,tjn->tn", w, D.reshape(T, topk, -1))

@@ -27,6 +27,7 @@ TAG_W = 2
 TAG_OUTLIER = 3
 TAG_BIAS = 4
 TAG_TOPK = 5
+TAG_GATE = 6
 
 E4M3_MAX = 448.0
 
@@ -134,3 +135,11 @@ def zipf_topk_ids(T: int, E: int, topk: int, alpha: float = 1.1, seed: int = 0) 
     keys = logp[None, :] + g
     order = np.argsort(-keys, axis=1, kind="stable")[:, :topk]
     return torch.from_numpy(order.astype(np.int32))
+
+
+def topk_weights(T: int, topk: int, seed: int = 0) -> torch.Tensor:
+    """Router gate weights ``[T, topk]`` float32: a softmax over ``topk``
+    standard-normal logits per token (positive, each row sums to about 1)."""
+    z = rng(seed, TAG_GATE).standard_normal(size=(T, topk)).astype(np.float32)
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return torch.from_numpy((e / e.sum(axis=1, keepdims=True)).astype(np.float32))

@@ -135,5 +135,10 @@ def test_moe_and_grouped_validation(q8):
     assert q8._gmm(*g(64, 500)) == q8.Q8_ESHAPE
     assert q8._gmm(*g(64, 512, cmap=8)) == q8.Q8_EWORKSPACE
     assert q8._gmm(*g(0, 512)) == q8.Q8_OK
+    assert q8._fin(p, q8.Q8_F32, p, p, 4, 2, 16, p, p) == q8.Q8_EINVAL        # dtype
+    assert q8._fin(p, q8.Q8_BF16, p, p, 4, 0, 16, p, p) == q8.Q8_ESHAPE       # topk
+    assert q8._fin(p, q8.Q8_BF16, p, p, 4, 2, 16, p, p) == q8.Q8_EINVAL       # null D / out
+    assert q8._fin(p, q8.Q8_BF16, p, p, 0, 2, 16, p, p) == q8.Q8_OK           # T = 0
+    assert q8._fin(p, q8.Q8_BF16, p, p, 1 << 30, 4, 16, p, p) == q8.Q8_ESHAPE # T * topk
     assert q8._shuf(p, 16, p, 4, p, p) == q8.Q8_EINVAL
     assert q8._shuf(p, 16, p, 0, p, p) == q8.Q8_OK

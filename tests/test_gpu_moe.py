@@ -145,3 +145,68 @@ def test_grouped_single_expert_equals_dense():
     dense = m.blockwise_scaled_mm(aq, W[0].to(DEV), As, Ws[0].to(DEV))
     sync()
     assert torch.equal(d, dense)
+
+
+def finalize_bound(w, D_rows, ref):
+    """|out - ref| <= 2^-8 |ref| (the 16-bit output rounding) + 2^-20 sum|w d|
+    (float32 accumulation over the top-k terms)."""
+    mag = np.einsum("tj,tjn->tn", np.abs(w), np.abs(D_rows))
+    return 2.0 ** -8 * np.abs(ref) + 2.0 ** -20 * mag
+
+
+@pytest.mark.parametrize("T,topk,N,dtype,perm,weights", [
+    (4096, 8, 2048, "bf16", True, True), (4096, 8, 2048, "bf16", False, True),
+    (37, 3, 100, "f16", True, True), (5, 2, 24, "bf16", False, False), (70000, 1, 16, "bf16", True, True)])
+def test_finalize_parity(T, topk, N, dtype, perm, weights):
+    """Synthetic routed rows and gate weights on both sides; with ``perm`` the
+    rows are in expert-sorted order and the routing table names them."""
+    m = q8()
+    D = synth.activations(T * topk, N, dtype, seed=T + N)
+    w = synth.topk_weights(T, topk, seed=T) if weights else None
+    op = None
+    if perm:
+        ids = synth.zipf_topk_ids(T, max(topk, 16), topk, seed=T)
+        op = om.moe_mm_data(ids.numpy(), max(topk, 16), N, N)[4]
+    out = m.moe_finalize(D.to(DEV), None if w is None else w.to(DEV), topk,
+                         None if op is None else torch.from_numpy(op).to(DEV))
+    sync()
+    Dn = D.double().numpy()
+    wn = None if w is None else w.double().numpy()
+    ref = om.finalize(Dn, wn, topk, op)
+    rows = om.unpermute(Dn, op) if perm else Dn
+    got = out.double().cpu().numpy()
+    bound = finalize_bound(np.ones((T, topk)) if wn is None else wn, rows.reshape(T, topk, N), ref)
+    assert np.all(np.abs(got - ref) <= bound)
+
+
+def test_moe_step_with_finalize():
+    """Routing, quant, grouped GEMM into expert-sorted rows (no scatter), then
+    the finalize with the output permutation, against the oracle path."""
+    m = q8()
+    T, E, topk, N, K, bk = 96, 8, 4, 256, 512, 128
+    ids = synth.zipf_topk_ids(T, E, topk, seed=7)
+    x = synth.activations(T, K, "bf16", seed=7)
+    W, Ws = synth.fp8_block_weights(N, K, bk, bk, experts=E, seed=7)
+    w = synth.topk_weights(T, topk, seed=7)
+    off, ps1, _, ip, op = gpu_routing(ids.to(DEV), E, N, K)
+    aq = torch.empty((T, K), dtype=torch.float8_e4m3fn, device=DEV)
+    As = torch.empty((T, K // bk), dtype=torch.float32, device=DEV)
+    m.quant_8bit(x.to(DEV), aq, As, bk, EPS, -448.0, 448.0, False)
+    d_sorted = torch.empty((T * topk, N), dtype=torch.bfloat16, device=DEV)
+    m.grouped_blockwise_scaled_mm(d_sorted, aq, W.to(DEV), As, Ws.to(DEV), off, ps1, a_map=ip)
+    out = m.moe_finalize(d_sorted, w.to(DEV), topk, op)
+    sync()
+    aq_o, as_o = oq.per_token_group(x.float().numpy(), bk, EPS, -448.0, 448.0, False, "e4m3")
+    off_o, _, _, ip_o, op_o = om.moe_mm_data(ids.numpy(), E, N, K)
+    d_ref = om.grouped_blockwise_scaled_mm(aq_o, as_o, W.numpy(), Ws.numpy(), off_o, ip_o, bk, bk)
+    wn = w.double().numpy()
+    ref = om.finalize(d_ref, wn, topk, op_o)
+    # each routed row carries the GEMM tolerance and its rounding to bf16
+    # (relative 2^-9); the sum adds float32 accumulation and the final bf16
+    # rounding (relative 2^-9, 2^-8 with margin)
+    rows = om.unpermute(d_ref, op_o).reshape(T, topk, N)
+    rms = float(np.sqrt(np.mean(d_ref * d_ref)))
+    per_row = 1e-2 * np.abs(rows) + 1e-3 * rms + 2.0 ** -9 * np.abs(rows)
+    bound = np.einsum("tj,tjn->tn", np.abs(wn), per_row) + 2.0 ** -8 * np.abs(ref)
+    got = out.double().cpu().numpy()
+    assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) / bound))

@@ -108,3 +108,39 @@ def test_grouped_single_expert_is_one_gemm():
     off, _, _, inp, outp = moe.moe_mm_data(ids, E, N, K)
     out = moe.unpermute(moe.grouped_blockwise_scaled_mm(Aq, As, W, Ws, off, inp, bk, bk), outp)
     assert np.array_equal(out, gemm.blockwise_scaled_mm(Aq, As, W[0], Ws[0], bk, bk))
+
+
+def test_finalize_brute_force_and_permutation_fusion():
+    """Python-loop brute force, and the fused form (expert-sorted rows named
+    by output_permutation) equals un-permuting first."""
+    from oracle import moe
+    r = np.random.default_rng(41)
+    T, topk, E, N = 9, 3, 5, 7
+    ids = np.stack([r.choice(E, size=topk, replace=False) for _ in range(T)]).astype(np.int32)
+    off, ps1, ps2, ip, op = moe.moe_mm_data(ids, E, N, 4)
+    D_sorted = r.standard_normal((T * topk, N))
+    w = r.uniform(0.0, 1.0, size=(T, topk))
+    fused = moe.finalize(D_sorted, w, topk, op)
+    D_unperm = moe.unpermute(D_sorted, op)
+    plain = moe.finalize(D_unperm, w, topk)
+    assert np.array_equal(fused, plain)
+    for t in range(T):
+        for n in range(N):
+            ref = 0.0
+            for j in range(topk):
+                ref += w[t, j] * D_unperm[t * topk + j, n]
+            assert abs(plain[t, n] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def test_finalize_special_cases():
+    from oracle import moe
+    r = np.random.default_rng(42)
+    D = r.standard_normal((8, 5))
+    # top-1 with weight 1 is the identity; no weights sums the top-k rows
+    assert np.array_equal(moe.finalize(D, np.ones((8, 1)), 1), D)
+    assert np.array_equal(moe.finalize(D, None, 2), D[0::2] + D[1::2])
+    # one-hot weights pick a row exactly
+    w = np.zeros((4, 2)); w[:, 1] = 1.0
+    assert np.array_equal(moe.finalize(D, w, 2), D[1::2])
+    with pytest.raises(ValueError):
+        moe.finalize(D[:7], None, 2)
