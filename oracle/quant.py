@@ -93,3 +93,77 @@ def static(x, scale: float, qmin: float, qmax: float, qdtype: str = "e4m3"):
     """Given scale -> codes (the scale itself is an input, not an output)."""
     x32 = np.asarray(x, dtype=F32)
     return _quantize_with_scale(x32, F32(scale), qmin, qmax, qdtype)
+
+
+# ---- fused SiLU-and-mul + quant, masked rows ---------------------------------
+# "Implementation: Sgl project Sglang GEMM Interface", Description ›
+# Quantization Routines: sgl_per_token_group_quant_8bit has a variant with a
+# fused SiLU-and-mul and masked-M support (arguments fuse_silu_and_mul and
+# masked_m in its signature). The page gives no formula; the readings taken:
+#
+# * SiLU-and-mul of a row [gate | up] of width 2K is y = silu(gate) * up with
+#   silu(g) = g / (1 + exp(-g)), the first half the gate and the second half
+#   the multiplier (the gated-MLP convention of the MoE pages' activations);
+# * y is evaluated in IEEE float32, one rounding per operation, in the order
+#   e = exp(-g), d = 1 + e, h = g / d, y = h * up, where exp is the correctly
+#   rounded float32 exponential. Every step is then an exactly defined float32
+#   operation, so the code decided from y is unique;
+# * masked rows: the input is E blocks of max_m rows ([E, max_m, .] flattened)
+#   and masked_m[e] rows of block e are valid; the other rows are neither read
+#   nor written.
+
+
+def exp_rn32(x) -> np.ndarray:
+    """Correctly rounded float32 exp of float32 inputs.
+
+    numpy's float64 exp (error well below a float64 ulp) rounded once to
+    float32: the float32 result is the correctly rounded one unless the exact
+    value lies within about 2^-52 (relative) of a float32 rounding midpoint;
+    tests/test_oracle_quant.py checks every bf16 input against an exact
+    decimal computation. Overflow gives +inf and deep underflow +0, as IEEE
+    rounding of the exact value does."""
+    x64 = np.asarray(x, dtype=F32).astype(np.float64)
+    with np.errstate(over="ignore"):
+        return np.exp(x64).astype(F32)
+
+
+def silu_and_mul(x, K: int | None = None) -> np.ndarray:
+    """``x [M, 2K]`` (gate | up) -> ``y [M, K]`` float32 (readings above)."""
+    x32 = np.asarray(x, dtype=F32)
+    if K is None:
+        if x32.shape[1] % 2:
+            raise ValueError("silu_and_mul: odd row width")
+        K = x32.shape[1] // 2
+    g, u = x32[:, :K], x32[:, K:2 * K]
+    with np.errstate(over="ignore", invalid="ignore"):
+        e = exp_rn32(-g)
+        d = (F32(1.0) + e).astype(F32)
+        h = (g / d).astype(F32)
+        return (h * u).astype(F32)
+
+
+def masked_rows(M: int, masked_m, max_m: int) -> np.ndarray:
+    """Boolean [M]: row r is valid iff r % max_m < masked_m[r // max_m]."""
+    mm = np.asarray(masked_m, dtype=np.int64)
+    if max_m <= 0 or M % max_m != 0 or mm.size != M // max_m:
+        raise ValueError("masked rows: M must be len(masked_m) * max_m")
+    r = np.arange(M)
+    return (r % max_m) < mm[r // max_m]
+
+
+def per_token_group_fused(x, group_size: int, eps: float, qmin: float, qmax: float,
+                          scale_ue8m0: bool = False, qdtype: str = "e4m3",
+                          silu: bool = False, masked_m=None, max_m: int | None = None):
+    """Per-token-group quant of ``silu_and_mul(x)`` (or of ``x``) on the valid
+    rows. Returns ``(q, s, valid)``; rows where ``valid`` is False hold zeros
+    here and are left untouched by the GPU library."""
+    x32 = np.asarray(x, dtype=F32)
+    y = silu_and_mul(x32) if silu else x32
+    M = y.shape[0]
+    valid = np.ones(M, dtype=bool) if masked_m is None else masked_rows(M, masked_m, max_m)
+    q = np.zeros(y.shape, dtype=np.uint8 if qdtype == "e4m3" else np.int8)
+    s = np.zeros((M, y.shape[1] // group_size), dtype=F32)
+    if valid.any():
+        qv, sv = per_token_group(y[valid], group_size, eps, qmin, qmax, scale_ue8m0, qdtype)
+        q[valid], s[valid] = qv, sv
+    return q, s, valid
