@@ -235,6 +235,47 @@ def bench_quant(torch, q8, synth, reps):
     return res
 
 
+def bench_silu_quant(torch, q8, synth, reps):
+    """Fused SiLU-and-mul + group-128 FP8 quant. Dense: [4096, 2 x 7168] bf16
+    -> [4096, 7168] codes (inputs rotated past the Infinity Cache). Masked:
+    the expert-major layout [64, max_m, 2 x 1024] of the 4096-token top-8
+    routing (per-expert counts from the same Zipf ids as the MoE step,
+    max_m = the largest count), only the routed rows valid."""
+    dev = "cuda:0"
+    res = {}
+    M, K, g = 4096, 7168, 128
+    nbytes = M * 2 * K * 2 + M * K + M * (K // g) * 4
+    copies = max(2, -(-(MALL_BYTES + (64 << 20)) // (M * 2 * K * 2)))
+    base = synth.activations(M, 2 * K, "bf16", seed=0).to(dev)
+    xs = [base.clone() for _ in range(copies)]
+    aq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+    As = torch.empty((M, K // g), dtype=torch.float32, device=dev)
+    u = batched_us(torch, lambda c: q8.quant_8bit(xs[c], aq, As, g, EPS, -448.0, 448.0, False,
+                                                  fuse_silu_and_mul=True), copies, reps)
+    gbs = nbytes / (u["median"] * 1e-6) / 1e9
+    res["dense_4096x7168_g128"] = {"us": round(u["median"], 3), "algorithmic_bytes": nbytes,
+                                   "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    del xs, base
+    T, E, topk, I = 4096, 64, 8, 1024
+    ids = synth.zipf_topk_ids(T, E, topk, seed=0)
+    counts = torch.bincount(ids.flatten().long(), minlength=E).to(torch.int32)
+    max_m = int(counts.max())
+    x3 = synth.activations(E * max_m, 2 * I, "bf16", seed=1).reshape(E, max_m, 2 * I).to(dev)
+    mm = counts.to(dev)
+    q3 = torch.empty((E, max_m, I), dtype=torch.float8_e4m3fn, device=dev)
+    s3 = torch.empty((E, max_m, I // g), dtype=torch.float32, device=dev)
+    u = batched_us(torch, lambda c: q8.quant_8bit(x3, q3, s3, g, EPS, -448.0, 448.0, False,
+                                                  fuse_silu_and_mul=True, masked_m=mm), 4, reps)
+    rows = int(counts.sum())
+    mbytes = rows * (2 * I * 2 + I + (I // g) * 4)
+    gbs = mbytes / (u["median"] * 1e-6) / 1e9
+    res["masked_e64_top8_I1024_g128"] = {"us": round(u["median"], 3), "valid_rows": rows,
+                                         "max_m": max_m, "algorithmic_bytes": mbytes,
+                                         "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    res["input_copies_rotated"] = copies
+    return res
+
+
 def bench_int8(torch, q8, synth, reps):
     M, N, K = 2048, 8192, 8192
     dev = "cuda:0"
@@ -445,6 +486,8 @@ def main() -> int:
         log(f"decode: {json.dumps(paths['decode_block32'])}")
         paths["quant_4096x7168"] = bench_quant(torch, q8, synth, 30)
         log(f"quant: {json.dumps(paths['quant_4096x7168'])}")
+        paths["silu_quant"] = bench_silu_quant(torch, q8, synth, 30)
+        log(f"silu quant: {json.dumps(paths['silu_quant'])}")
         paths["int8_2048x8192x8192"] = bench_int8(torch, q8, synth, reps)
         log(f"int8: {json.dumps(paths['int8_2048x8192x8192'])}")
         paths["fp8_per_token_x_channel_4096x7168x7168"] = bench_fp8_scaled(torch, q8, synth, reps)

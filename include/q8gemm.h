@@ -70,7 +70,7 @@ const char* q8gemm_last_error(void);
  * quantization of the vLLM scaled_mm page (AiterInt8ScaledMMLinearKernel).
  *
  * x       [M, K] of x_dtype (Q8_F32, Q8_BF16 or Q8_F16), row stride ld_x >= K
- *         elements.
+ *         elements ([M, 2K], ld_x >= 2K, with fuse_silu_and_mul).
  * q       [M, K] of q_dtype (Q8_E4M3FN or Q8_I8), contiguous (row stride K).
  * s       Q8_SCALE_PER_GROUP: output, [M, K/group_size] float32 row-major.
  *         Q8_SCALE_PER_TENSOR_DYNAMIC: output, s[0].
@@ -83,8 +83,23 @@ const char* q8gemm_last_error(void);
  * eps > 0 floors a (an all-zero group gets s = eps/qmax and zero codes).
  * Typical ranges: FP8 qmin=-448, qmax=448; INT8 qmin=-128, qmax=127.
  * scale_ue8m0 must be 0 with Q8_SCALE_STATIC.
- * fuse_silu_and_mul must be 0 and masked_m NULL (not implemented:
- * Q8_EUNSUPPORTED).
+ *
+ * Fused SiLU-and-mul and masked rows (the same page names a second version of
+ * the per-token-group quantizer that fuses the gated activation and honours
+ * a per-expert row count; Q8_SCALE_PER_GROUP only, else Q8_EUNSUPPORTED):
+ * fuse_silu_and_mul = 1: x is [M, 2K] (row stride ld_x >= 2K), each row
+ *   [gate | up]; the value quantized is y = silu(gate) * up, evaluated in
+ *   float32 one rounding per step: e = exp(-g) correctly rounded, d = 1 + e,
+ *   h = g / d (true division), y = h * u. q and s are [M, K] and
+ *   [M, K/group_size] as above. 0 quantizes x itself.
+ * masked_m != NULL: the M rows are E = M / max_m blocks of max_m rows (a
+ *   [E, max_m, .] tensor) and masked_m [E] int32 (device) holds the number
+ *   of valid leading rows of each block; row r is quantized only if
+ *   r % max_m < masked_m[r / max_m]. Other rows of q and s are not written
+ *   and their inputs are not read. Needs max_m >= 1 dividing M, M < 2^32.
+ *   Device precondition: 0 <= masked_m[e] <= max_m (larger values act as
+ *   max_m, negative values as 0). max_m is ignored when masked_m is NULL.
+ *
  * workspace: Q8_SCALE_PER_TENSOR_DYNAMIC needs quant_8bit_workspace_size()
  * bytes (partial maxima); other modes need none (NULL, 0 allowed).
  * M == 0 or K == 0 is a no-op.
@@ -94,7 +109,7 @@ int quant_8bit(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, int64_t ld
                void* q, q8_dtype q_dtype, float* s, int64_t group_size,
                q8_scale_mode mode, float eps, float qmin, float qmax,
                int scale_ue8m0, int fuse_silu_and_mul, const int32_t* masked_m,
-               void* workspace, size_t workspace_bytes, hipStream_t stream);
+               int64_t max_m, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Block-scaled FP8 GEMM with bf16/f16 output.

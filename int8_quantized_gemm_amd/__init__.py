@@ -61,7 +61,7 @@ def _sig(name, res, *args):
 _lib_last_error = _sig("q8gemm_last_error", ctypes.c_char_p)
 _quant_ws = _sig("quant_8bit_workspace_size", _sz, _i64, _i64, _i)
 _quant = _sig("quant_8bit", _i, _p, _i, _i64, _i64, _i64, _p, _i, _p, _i64, _i, _f, _f, _f, _i, _i,
-              _p, _p, _sz, _p)
+              _p, _i64, _p, _sz, _p)
 _bmm_ws = _sig("blockwise_scaled_mm_workspace_size", _sz, _i64, _i64, _i64, _i, _i)
 _bmm = _sig("blockwise_scaled_mm", _i, _p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i, _i, _p,
             _sz, _p)
@@ -160,19 +160,39 @@ def quant_8bit(input: torch.Tensor, output_q: torch.Tensor, output_s: torch.Tens
     float8_e4m3fn/uint8 codes or int8, ``output_s`` [M, K // group_size]
     float32 (``[1]`` for the per-tensor modes; an input for SCALE_STATIC).
     For INT8 pass ``fp8_min=-128, fp8_max=127``.
+
+    ``fuse_silu_and_mul``: ``input`` is [..., 2K] (rows [gate | up]) and the
+    codes are of ``silu(gate) * up``. ``masked_m`` (int32 [E]): ``input`` is
+    3-D [E, max_m, .] and only the first ``masked_m[e]`` rows of block ``e``
+    are quantized; the other rows of the outputs are left as they were.
     """
     dev = _dev(input, output_q, output_s, masked_m)
+    max_m = 0
+    if masked_m is not None:
+        if input.dim() != 3 or masked_m.dtype != torch.int32 or masked_m.numel() != input.shape[0]:
+            raise ValueError("masked_m needs a 3-D input [E, max_m, .] and int32 masked_m [E]")
+        _contig(masked_m)
+        E, max_m = input.shape[0], input.shape[1]
+        if input.stride(1) * max_m != input.stride(0) and E > 1:
+            raise ValueError("masked input blocks must be evenly strided rows")
+        input = input.reshape(E * max_m, input.shape[2]) if input.is_contiguous() else \
+            input.as_strided((E * max_m, input.shape[2]), (input.stride(1), input.stride(2)))
+        output_q = output_q.reshape(E * max_m, -1)
+        output_s = output_s.reshape(E * max_m, -1)
     if input.dim() != 2 or input.stride(1) != 1:
         raise ValueError("input must be 2-D with unit column stride")
     _contig(output_q, output_s)
-    M, K = input.shape
+    M, Kin = input.shape
+    K = Kin // 2 if fuse_silu_and_mul else Kin
+    if fuse_silu_and_mul and Kin % 2:
+        raise ValueError("fuse_silu_and_mul needs an even input width")
     if tuple(output_q.shape) != (M, K):
-        raise ValueError("output_q must have the input's shape")
+        raise ValueError("output_q must be [M, K] (K = half the input width when fused)")
     ws, wsb = _workspace(dev, _quant_ws(M, K, mode))
-    _check(_quant(_ptr(input), _dt(input.dtype), M, K, input.stride(0) if M > 1 else K,
+    _check(_quant(_ptr(input), _dt(input.dtype), M, K, input.stride(0) if M > 1 else Kin,
                   _ptr(output_q), _dt(output_q.dtype), _ptr(output_s), group_size, mode, eps,
                   fp8_min, fp8_max, int(scale_ue8m0), int(fuse_silu_and_mul), _ptr(masked_m),
-                  ws, wsb, _stream(dev)))
+                  max_m, ws, wsb, _stream(dev)))
 
 
 def blockwise_scaled_mm(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torch.Tensor,

@@ -64,11 +64,13 @@ size_t quant_8bit_workspace_size(int64_t M, int64_t K, q8_scale_mode mode) {
 int quant_8bit(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, int64_t ld_x, void* q,
                q8_dtype q_dtype, float* s, int64_t group_size, q8_scale_mode mode, float eps,
                float qmin, float qmax, int scale_ue8m0, int fuse_silu_and_mul,
-               const int32_t* masked_m, void* workspace, size_t workspace_bytes,
+               const int32_t* masked_m, int64_t max_m, void* workspace, size_t workspace_bytes,
                hipStream_t stream) {
   static const char* fn = "quant_8bit";
-  if (fuse_silu_and_mul) return fail(Q8_EUNSUPPORTED, "%s: fuse_silu_and_mul is not implemented", fn);
-  if (masked_m) return fail(Q8_EUNSUPPORTED, "%s: masked_m is not implemented", fn);
+  if (fuse_silu_and_mul != 0 && fuse_silu_and_mul != 1)
+    return fail(Q8_EINVAL, "%s: fuse_silu_and_mul must be 0 or 1", fn);
+  if ((fuse_silu_and_mul || masked_m) && mode != Q8_SCALE_PER_GROUP)
+    return fail(Q8_EUNSUPPORTED, "%s: fuse_silu_and_mul and masked_m need per-group scales", fn);
   if (x_dtype != Q8_F32 && x_dtype != Q8_BF16 && x_dtype != Q8_F16)
     return fail(Q8_EINVAL, "%s: x_dtype must be F32, BF16 or F16", fn);
   if (q_dtype != Q8_E4M3FN && q_dtype != Q8_I8)
@@ -76,7 +78,16 @@ int quant_8bit(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, int64_t ld
   if (mode != Q8_SCALE_PER_GROUP && mode != Q8_SCALE_PER_TENSOR_DYNAMIC && mode != Q8_SCALE_STATIC)
     return fail(Q8_EINVAL, "%s: unknown scale mode %d", fn, (int)mode);
   if (M < 0 || K < 0) return fail(Q8_ESHAPE, "%s: negative size", fn);
-  if (ld_x < K) return fail(Q8_ESHAPE, "%s: ld_x (%lld) < K (%lld)", fn, (long long)ld_x, (long long)K);
+  if (ld_x < (fuse_silu_and_mul ? 2 * K : K))
+    return fail(Q8_ESHAPE, "%s: ld_x (%lld) < input row width (%lld)", fn, (long long)ld_x,
+                (long long)(fuse_silu_and_mul ? 2 * K : K));
+  if (masked_m) {
+    if (max_m < 1 || M % max_m != 0)
+      return fail(Q8_ESHAPE, "%s: masked_m needs max_m >= 1 dividing M (M=%lld, max_m=%lld)", fn,
+                  (long long)M, (long long)max_m);
+    if (max_m > 0x7FFFFFFFLL || M > 0xFFFFFFFFLL)
+      return fail(Q8_ESHAPE, "%s: masked rows are indexed in 32 bits", fn);
+  }
   if (!(qmax > 0.0f) || !(qmin < 0.0f))
     return fail(Q8_EINVAL, "%s: need qmin < 0 < qmax", fn);
   if (q_dtype == Q8_E4M3FN && (qmax > 448.0f || qmin < -448.0f))
@@ -98,7 +109,7 @@ int quant_8bit(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, int64_t ld
   if (need && (!workspace || workspace_bytes < need))
     return fail(Q8_EWORKSPACE, "%s: workspace needs %zu bytes", fn, need);
   q8::QuantArgs a{x, x_dtype, M, K, ld_x, q, q_dtype, s, group_size, mode, eps, qmin, qmax,
-                  scale_ue8m0, workspace};
+                  scale_ue8m0, workspace, fuse_silu_and_mul, masked_m, masked_m ? max_m : 0};
   return hip_status(q8::launch_quant(a, stream), fn);
 }
 

@@ -16,6 +16,9 @@ struct QuantArgs {
   void* q; q8_dtype q_dtype; float* s; int64_t group_size;
   q8_scale_mode mode; float eps, qmin, qmax; int ue8m0;
   void* workspace;
+  int silu;                  // x rows are [gate | up], 2K wide
+  const int32_t* masked_m;   // [M / max_m] valid rows per block, or null
+  int64_t max_m;
 };
 size_t quant_partials_count(int64_t M, int64_t K);
 hipError_t launch_quant(const QuantArgs& a, hipStream_t stream);

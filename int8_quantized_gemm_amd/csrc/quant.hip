@@ -24,6 +24,9 @@
 //   quant_group_block  any other group size (odd sizes, unaligned strides,
 //                      longer rows): one workgroup per group, block reduction,
 //                      then a second pass that re-reads the group (L2 hit).
+//   quant_fused_wave,  fused SiLU-and-mul (y = silu(gate) * up) and/or masked
+//   quant_fused_block  rows: groups of 16..512 (power of two) per lane group,
+//                      any other group size one workgroup per group.
 //   amax_partials +    per-tensor dynamic: per-workgroup maxima into the
 //   quant_tensor       workspace, then every workgroup reduces them (the max
 //                      is order independent, so the result is deterministic)
@@ -381,6 +384,184 @@ __global__ __launch_bounds__(kThreads) void quant_tensor(
   }
 }
 
+// ---- fused SiLU-and-mul and masked rows ---------------------------------------
+// "Implementation: Sgl project Sglang GEMM Interface", Quantization Routines:
+// the per-token-group quantizer's variant with a fused SiLU-and-mul and
+// masked-M support. A row of the input is [gate | up] (2K wide); the value
+// quantized is y = silu(gate) * up, evaluated in float32 as
+//   e = exp(-g) (correctly rounded), d = 1 + e, h = g / d (IEEE), y = h * u,
+// one rounding per step, so y (and the code decided from it) is unique.
+// Masked rows: the M rows are E blocks of max_m; row r is processed only if
+// r % max_m < masked_m[r / max_m], other rows are neither read nor written.
+
+// Correctly rounded float32 exp. exp(x) = 2^k * exp(r) with k = rint(x / ln2)
+// and r = x - k ln2 (ln2 split into two doubles, |r| <= ln2/2), exp(r) from
+// its Taylor series to degree 13 in float64 (truncation below 2^-57, Horner
+// rounding about 2^-52), then one rounding to float32: the result is the
+// correctly rounded one unless exp(x) lies within ~2^-50 (relative) of a
+// float32 rounding midpoint; the parity tests check every bf16 input.
+// x is clamped to [-104, 89]: exp(89) overflows float32 and exp(-104) is below
+// half the smallest subnormal, so the float64 -> float32 conversion of the
+// clamped value gives +inf and +0 exactly as the unclamped value would.
+__device__ __forceinline__ float exp_rn32(float x) {
+  constexpr double kInvLn2 = 0x1.71547652b82fep+0;
+  constexpr double kLn2Hi = 0x1.62e42fefa39efp-1;   // ln 2 rounded to double
+  constexpr double kLn2Lo = 0x1.abc9e3b39803fp-56;  // ln 2 - kLn2Hi
+  const double xd = (double)__builtin_amdgcn_fmed3f(x, -104.0f, 89.0f);
+  const double k = __builtin_rint(xd * kInvLn2);
+  double r = __builtin_fma(-k, kLn2Hi, xd);
+  r = __builtin_fma(-k, kLn2Lo, r);
+  // 1/n! for n = 13 .. 2, rounded to double
+  double p = 0x1.6124613a86d09p-33;
+  p = __builtin_fma(p, r, 0x1.1eed8eff8d898p-29);
+  p = __builtin_fma(p, r, 0x1.ae64567f544e4p-26);
+  p = __builtin_fma(p, r, 0x1.27e4fb7789f5cp-22);
+  p = __builtin_fma(p, r, 0x1.71de3a556c734p-19);
+  p = __builtin_fma(p, r, 0x1.a01a01a01a01ap-16);
+  p = __builtin_fma(p, r, 0x1.a01a01a01a01ap-13);
+  p = __builtin_fma(p, r, 0x1.6c16c16c16c17p-10);
+  p = __builtin_fma(p, r, 0x1.1111111111111p-7);
+  p = __builtin_fma(p, r, 0x1.5555555555555p-5);
+  p = __builtin_fma(p, r, 0x1.5555555555555p-3);
+  p = __builtin_fma(p, r, 0.5);
+  p = __builtin_fma(p, r, 1.0);
+  p = __builtin_fma(p, r, 1.0);
+  return (float)__builtin_ldexp(p, (int)k);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float d = 1.0f + exp_rn32(-g);
+  const float h = g / d;  // IEEE division (correctly rounded)
+  return h * u;
+}
+
+// Is row r live under the mask? (masked_m == nullptr: every row.)
+__device__ __forceinline__ bool row_live(const int32_t* __restrict__ masked_m, uint32_t max_m,
+                                         uint32_t row) {
+  if (!masked_m) return true;
+  const uint32_t e = row / max_m;
+  return (int64_t)(row - e * max_m) < (int64_t)masked_m[e];
+}
+
+// Groups of 16 * TPG elements (16..512): each lane owns 16 consecutive outputs
+// of one row (gate and up vectors loaded with 16-byte loads), the group's TPG
+// lanes are adjacent and reduce their |max| with xor shuffles. Rows are
+// addressed through ld_x (the input is [M, 2K] with SILU, [M, K] without),
+// the codes and scales are contiguous. The host keeps M * K / 16 below 2^32.
+template <int XT, bool FP8, bool UE, int TPG, bool SILU>
+__global__ __launch_bounds__(kThreads) void quant_fused_wave(
+    const void* __restrict__ x, int64_t M, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
+    float* __restrict__ s, const int32_t* __restrict__ masked_m, uint32_t max_m, float eps,
+    float qmin, float qmax) {
+  const uint32_t vpr = (uint32_t)(K / 16);
+  const uint32_t total = (uint32_t)(M * vpr);
+  const uint32_t v = blockIdx.x * kThreads + threadIdx.x;
+  // lanes past the end stand in for the last vector (groups are wholly in or
+  // out of range: total is a multiple of TPG)
+  const uint32_t vv = v < total ? v : total - 1;
+  const uint32_t row = vv / vpr;
+  const bool live = v < total && row_live(masked_m, max_m, row);
+  // a wave holds whole groups, so a wave with no live lane has nothing to do
+  // (masked layouts are mostly dead rows)
+  if (__ballot(live) == 0) return;
+  float y[2][8];
+  if (live) {
+    const int64_t off = (int64_t)row * ld_x + (int64_t)(vv - row * vpr) * 16;
+    load8<XT>(x, off, y[0]);
+    load8<XT>(x, off + 8, y[1]);
+    if constexpr (SILU) {
+      float u[2][8];
+      load8<XT>(x, off + K, u[0]);
+      load8<XT>(x, off + K + 8, u[1]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[h][i] = silu_mul(y[h][i], u[h][i]);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[h][i] = 0.0f;
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(y[h][i]));
+  a = wave_max_xor(a, TPG);  // every lane takes part; dead lanes add 0
+  if (!live) return;
+  const float sc = group_scale<UE>(a, eps, qmax);
+  const Divider<UE> div(sc);
+  float c0[8], c1[8];
+  div.apply8(y[0], c0, qmin, qmax);
+  div.apply8(y[1], c1, qmin, qmax);
+  const uint2 lo = encode8<FP8>(c0), hi = encode8<FP8>(c1);
+  *reinterpret_cast<uint4*>(q + (int64_t)v * 16) = uint4{lo.x, lo.y, hi.x, hi.y};
+  if ((v & (TPG - 1)) == 0) s[v / TPG] = sc;
+}
+
+// Any group size: one workgroup per group, element-wise loads, a block
+// reduction, then a second pass that recomputes y and writes the codes.
+template <int XT, bool FP8, bool UE, bool SILU>
+__global__ __launch_bounds__(kThreads) void quant_fused_block(
+    const void* __restrict__ x, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
+    float* __restrict__ s, int64_t g, const int32_t* __restrict__ masked_m, uint32_t max_m,
+    float eps, float qmin, float qmax) {
+  __shared__ float red[kThreads / kWave];
+  const int64_t groups_per_row = K / g;
+  const int64_t row = blockIdx.x / groups_per_row;
+  const int64_t j = blockIdx.x - row * groups_per_row;
+  if (!row_live(masked_m, max_m, (uint32_t)row)) return;  // uniform per workgroup
+  const int64_t xb = row * ld_x + j * g;
+  const int64_t qb = row * K + j * g;
+  auto value = [&](int64_t i) -> float {
+    const float gv = load1<XT>(x, xb + i);
+    if constexpr (SILU) return silu_mul(gv, load1<XT>(x, xb + K + i));
+    else return gv;
+  };
+  float a = 0.0f;
+  for (int64_t i = threadIdx.x; i < g; i += kThreads) a = fmaxf(a, fabsf(value(i)));
+  a = block_max(a, red);
+  const float sc = group_scale<UE>(a, eps, qmax);
+  if (threadIdx.x == 0) s[blockIdx.x] = sc;
+  const Divider<UE> div(sc);
+  for (int64_t i = threadIdx.x; i < g; i += kThreads) q[qb + i] = encode1<FP8>(div(value(i), qmin, qmax));
+}
+
+template <int XT, bool FP8, bool UE, bool SILU>
+hipError_t dispatch_fused(const QuantArgs& a, hipStream_t st) {
+  const int esz = XT == Q8_F32 ? 4 : 2;
+  const int64_t g = a.group_size;
+  uint8_t* q = static_cast<uint8_t*>(a.q);
+  const uint32_t max_m = a.masked_m ? (uint32_t)a.max_m : 1u;
+  const dim3 blk(kThreads);
+  const int64_t total = a.M * (a.K / 16);
+  const bool wave = g >= 16 && g <= 512 && (g & (g - 1)) == 0 && total < 0xFFFF0000LL &&
+                    (uintptr_t)a.x % 16 == 0 && (uintptr_t)q % 16 == 0 &&
+                    (a.ld_x * esz) % 16 == 0 && (a.K * esz) % 16 == 0;
+  if (wave) {
+    const dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
+    switch (g / 16) {
+#define Q8_FUSED_CASE(T)                                                                         \
+  case T:                                                                                        \
+    hipLaunchKernelGGL((quant_fused_wave<XT, FP8, UE, T, SILU>), grid, blk, 0, st, a.x, a.M, a.K, \
+                       a.ld_x, q, a.s, a.masked_m, max_m, a.eps, a.qmin, a.qmax);                \
+    break;
+      Q8_FUSED_CASE(1) Q8_FUSED_CASE(2) Q8_FUSED_CASE(4) Q8_FUSED_CASE(8) Q8_FUSED_CASE(16)
+      Q8_FUSED_CASE(32)
+#undef Q8_FUSED_CASE
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  const int64_t ngroups = a.M * (a.K / g);
+  if (ngroups > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((quant_fused_block<XT, FP8, UE, SILU>), dim3((unsigned)ngroups), blk, 0, st,
+                     a.x, a.K, a.ld_x, q, a.s, g, a.masked_m, max_m, a.eps, a.qmin, a.qmax);
+  return hipGetLastError();
+}
+
 // ---- host dispatch -------------------------------------------------------------
 template <int XT, bool FP8, bool UE>
 hipError_t dispatch(const QuantArgs& a, hipStream_t st) {
@@ -479,12 +660,19 @@ hipError_t dispatch(const QuantArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int XT, bool FP8, bool UE>
+hipError_t dispatch_any(const QuantArgs& a, hipStream_t st) {
+  if (a.silu) return dispatch_fused<XT, FP8, UE, true>(a, st);
+  if (a.masked_m) return dispatch_fused<XT, FP8, UE, false>(a, st);
+  return dispatch<XT, FP8, UE>(a, st);
+}
+
 template <int XT>
 hipError_t dispatch_q(const QuantArgs& a, hipStream_t st) {
   const bool ue = a.ue8m0 != 0 && a.mode != Q8_SCALE_STATIC;
   if (a.q_dtype == Q8_E4M3FN)
-    return ue ? dispatch<XT, true, true>(a, st) : dispatch<XT, true, false>(a, st);
-  return ue ? dispatch<XT, false, true>(a, st) : dispatch<XT, false, false>(a, st);
+    return ue ? dispatch_any<XT, true, true>(a, st) : dispatch_any<XT, true, false>(a, st);
+  return ue ? dispatch_any<XT, false, true>(a, st) : dispatch_any<XT, false, false>(a, st);
 }
 
 }  // namespace

@@ -61,27 +61,38 @@ def test_quant_validation(q8):
     L = q8._lib
     f, p = ctypes.c_float, None
     # bad input dtype
-    assert q8._quant(p, 7, 4, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 0, p, p, 0, p) == q8.Q8_EINVAL
+    assert q8._quant(p, 7, 4, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 0, p, 0, p, 0, p) == q8.Q8_EINVAL
     assert "x_dtype" in q8.last_error()
     # group does not divide K
-    assert q8._quant(p, q8.Q8_BF16, 4, 100, 100, p, q8.Q8_E4M3FN, p, 32, 0, 1e-10, -448, 448, 0, 0, p, p, 0, p) == q8.Q8_ESHAPE
+    assert q8._quant(p, q8.Q8_BF16, 4, 100, 100, p, q8.Q8_E4M3FN, p, 32, 0, 1e-10, -448, 448, 0, 0, p, 0, p, 0, p) == q8.Q8_ESHAPE
     # FP8 clip range beyond 448
-    assert q8._quant(p, q8.Q8_BF16, 4, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -480, 480, 0, 0, p, p, 0, p) == q8.Q8_EINVAL
-    # fused SiLU-and-mul, masked_m not implemented
-    assert q8._quant(p, q8.Q8_BF16, 4, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 1, p, p, 0, p) == q8.Q8_EUNSUPPORTED
-    assert q8._quant(p, q8.Q8_BF16, 4, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 0, 8, p, 0, p) == q8.Q8_EUNSUPPORTED
+    assert q8._quant(p, q8.Q8_BF16, 4, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -480, 480, 0, 0, p, 0, p, 0, p) == q8.Q8_EINVAL
+    # fused SiLU-and-mul: the input row is [gate | up], so ld_x must cover 2K
+    assert q8._quant(p, q8.Q8_BF16, 4, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 1, p, 0, p, 0, p) == q8.Q8_ESHAPE
+    assert "row width" in q8.last_error()
+    assert q8._quant(p, q8.Q8_BF16, 4, 128, 256, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 2, p, 0, p, 0, p) == q8.Q8_EINVAL
+    # fused / masked need per-group scales
+    assert q8._quant(8, q8.Q8_BF16, 4, 128, 256, 8, q8.Q8_E4M3FN, 8, 128, 1, 1e-10, -448, 448, 0, 1, p, 0, 8, 4096, p) == q8.Q8_EUNSUPPORTED
+    assert q8._quant(8, q8.Q8_BF16, 4, 128, 128, 8, q8.Q8_E4M3FN, 8, 128, 1, 1e-10, -448, 448, 0, 0, 8, 2, 8, 4096, p) == q8.Q8_EUNSUPPORTED
+    # masked rows: max_m must be >= 1 and divide M
+    assert q8._quant(8, q8.Q8_BF16, 4, 128, 128, 8, q8.Q8_E4M3FN, 8, 128, 0, 1e-10, -448, 448, 0, 0, 8, 0, p, 0, p) == q8.Q8_ESHAPE
+    assert q8._quant(8, q8.Q8_BF16, 6, 128, 128, 8, q8.Q8_E4M3FN, 8, 128, 0, 1e-10, -448, 448, 0, 0, 8, 4, p, 0, p) == q8.Q8_ESHAPE
+    assert "max_m" in q8.last_error()
+    # a valid fused + masked request with null data pointers stops at the null check
+    assert q8._quant(p, q8.Q8_BF16, 6, 128, 256, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 1, 8, 3, p, 0, p) == q8.Q8_EINVAL
+    assert "null" in q8.last_error()
     # ld_x < K
-    assert q8._quant(p, q8.Q8_BF16, 4, 128, 64, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 0, p, p, 0, p) == q8.Q8_ESHAPE
+    assert q8._quant(p, q8.Q8_BF16, 4, 128, 64, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 0, p, 0, p, 0, p) == q8.Q8_ESHAPE
     # null pointers with real work
-    assert q8._quant(p, q8.Q8_BF16, 4, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 0, p, p, 0, p) == q8.Q8_EINVAL
+    assert q8._quant(p, q8.Q8_BF16, 4, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 0, p, 0, p, 0, p) == q8.Q8_EINVAL
     # per-tensor dynamic needs workspace
     need = q8._quant_ws(4, 128, q8.SCALE_PER_TENSOR_DYNAMIC)
     assert need > 0 and q8._quant_ws(4, 128, q8.SCALE_PER_GROUP) == 0
-    assert q8._quant(8, q8.Q8_BF16, 4, 128, 128, 8, q8.Q8_E4M3FN, 8, 128, 1, 1e-10, -448, 448, 0, 0, p, p, 0, p) == q8.Q8_EWORKSPACE
+    assert q8._quant(8, q8.Q8_BF16, 4, 128, 128, 8, q8.Q8_E4M3FN, 8, 128, 1, 1e-10, -448, 448, 0, 0, p, 0, p, 0, p) == q8.Q8_EWORKSPACE
     # UE8M0 with a static scale is rejected
-    assert q8._quant(8, q8.Q8_BF16, 4, 128, 128, 8, q8.Q8_E4M3FN, 8, 128, 2, 1e-10, -448, 448, 1, 0, p, p, 0, p) == q8.Q8_EINVAL
+    assert q8._quant(8, q8.Q8_BF16, 4, 128, 128, 8, q8.Q8_E4M3FN, 8, 128, 2, 1e-10, -448, 448, 1, 0, p, 0, p, 0, p) == q8.Q8_EINVAL
     # empty input is a no-op (no pointer needed)
-    assert q8._quant(p, q8.Q8_BF16, 0, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 0, p, p, 0, p) == q8.Q8_OK
+    assert q8._quant(p, q8.Q8_BF16, 0, 128, 128, p, q8.Q8_E4M3FN, p, 128, 0, 1e-10, -448, 448, 0, 0, p, 0, p, 0, p) == q8.Q8_OK
     assert q8.last_error() == ""
 
 
