@@ -122,3 +122,26 @@ def scaled_mm_fp8(Aq, sa, Wq, sb, bias=None) -> np.ndarray:
     if bias is not None:
         D = D + np.asarray(bias, dtype=np.float64)[None, :]
     return D
+
+
+# ---- power-of-two (UE8M0) block scales ----------------------------------------
+# The vLLM scaled_mm page (XPUFp8BlockScaledMMKernel, process_weights_after_
+# loading) accepts weight scales stored as float8_e8m0fnu bytes and upcasts
+# them to float32; the block32 DeepGEMM PR keeps UE8M0 activation scales. An
+# E8M0 byte b holds the power of two 2^(b - 127) (b = 255 is NaN). With both
+# operands' block scales in that form the product is the same block-scaled
+# GEMM as above, with the decoded values as the scales.
+
+
+def e8m0_decode(b) -> np.ndarray:
+    """E8M0 bytes -> exact float64 values 2^(b - 127) (255 -> NaN)."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    v = np.ldexp(1.0, b - 127)
+    return np.where(b == 255, np.nan, v)
+
+
+def blockwise_scaled_mm_e8m0(Aq, As_b, Wq, Ws_b, bn: int, bias=None) -> np.ndarray:
+    """Block-scaled FP8 GEMM with E8M0 scales, 32-wide K blocks -> float64.
+
+    ``As_b [M, K/32]`` and ``Ws_b [ceil(N/bn), K/32]`` uint8 E8M0 bytes."""
+    return blockwise_scaled_mm(Aq, e8m0_decode(As_b), Wq, e8m0_decode(Ws_b), bn, 32, bias)

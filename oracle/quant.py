@@ -167,3 +167,17 @@ def per_token_group_fused(x, group_size: int, eps: float, qmin: float, qmax: flo
         qv, sv = per_token_group(y[valid], group_size, eps, qmin, qmax, scale_ue8m0, qdtype)
         q[valid], s[valid] = qv, sv
     return q, s, valid
+
+
+def e8m0_bytes(s) -> np.ndarray:
+    """Power-of-two float32 scales (UE8M0-rounded) -> their E8M0 bytes, the
+    biased exponent b with s = 2^(b - 127) (packed UE8M0 storage, the
+    float8_e8m0fnu scale dtype of the vLLM scaled_mm page)."""
+    s = np.asarray(s, dtype=F32)
+    m, e = np.frexp(s.astype(np.float64))        # s = m * 2^e, m in [0.5, 1)
+    if not np.all(m == 0.5):
+        raise ValueError("e8m0_bytes: scales must be powers of two")
+    b = e - 1 + 127
+    if np.any(b < 0) or np.any(b > 254):
+        raise ValueError("e8m0_bytes: exponent out of range")
+    return b.astype(np.uint8)

@@ -84,6 +84,32 @@ def _quantize_block_tile_rows(w: np.ndarray, bn: int, bk: int):
     return codes, ws
 
 
+def _pow2_at_least(x: np.ndarray) -> np.ndarray:
+    """Smallest power of two >= x (x > 0), via frexp: x = m 2^e, m in [0.5, 1)."""
+    m, e = np.frexp(x.astype(np.float64))
+    return np.ldexp(1.0, np.where(m == 0.5, e - 1, e)).astype(np.float32)
+
+
+def fp8_block_weights_e8m0(N: int, K: int, bn: int, bk: int = 32, sigma: float = 0.02,
+                           seed: int = 0, tag: int = TAG_W):
+    """Block-FP8 weights whose per-tile scales are powers of two, the way a
+    checkpoint with float8_e8m0fnu weight scales ships them: the scale of a
+    [bn, bk] tile is the smallest power of two >= tile amax / 448, the codes
+    are torch's e4m3fn cast of w / scale. Returns ``(Wq [N, K] uint8,
+    Ws_e8m0 [ceil(N/bn), ceil(K/bk)] uint8)`` with scale = 2^(byte - 127)."""
+    w = normal_f32((N, K), sigma, seed, tag)
+    nb, kb = -(-N // bn), -(-K // bk)
+    pad = np.zeros((nb * bn, kb * bk), dtype=np.float32)
+    pad[:N, :K] = np.abs(w)
+    amax = pad.reshape(nb, bn, kb, bk).max(axis=(1, 3))
+    ws = _pow2_at_least(np.maximum(amax, np.float32(1e-12)) / np.float32(E4M3_MAX))
+    full = np.repeat(np.repeat(ws, bn, axis=0), bk, axis=1)[:N, :K]
+    ratio = np.clip(w / full, -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    codes = torch.from_numpy(ratio).to(torch.float8_e4m3fn).view(torch.uint8)
+    exps = (ws.view(np.uint32) >> np.uint32(23)).astype(np.uint8)
+    return codes, torch.from_numpy(exps)
+
+
 def fp8_block_weights(N: int, K: int, bn: int, bk: int, sigma: float = 0.02,
                       seed: int = 0, tag: int = TAG_W, experts: int | None = None):
     """Checkpoint-style block-FP8 weights.
