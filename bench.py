@@ -276,6 +276,66 @@ def bench_silu_quant(torch, q8, synth, reps):
     return res
 
 
+def bench_e8m0(torch, q8, synth, reps):
+    """Block32 FP8 GEMMs with power-of-two (E8M0) scales on both operands (the
+    MX-scaled MFMA path): prefill 4096 x 7168 x 7168 and decode M in
+    {1, 4, 16, 64} x 4096 x 7168 (weights rotated past the Infinity Cache),
+    next to the float32-scale block32 kernel on the same prefill shape."""
+    dev = "cuda:0"
+    res = {}
+    M, N, K = 4096, 7168, 7168
+    x = synth.activations(M, K, "bf16", seed=0).to(dev)
+    aq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+    asb = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    q8.quant_8bit(x, aq, asb, 32, EPS, -448.0, 448.0, 2)
+    Wq, Wsb = synth.fp8_block_weights_e8m0(N, K, 32, 32, seed=0)
+    Wq, Wsb = Wq.to(dev), Wsb.to(dev)
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    t = KernelTimer(torch)
+    for i in range(reps + 3):
+        with (t if i >= 3 else _Null()):
+            q8.blockwise_scaled_mm_e8m0(aq, Wq, asb, Wsb, block_n=32, out=D)
+    torch.cuda.synchronize()
+    us = t.us()["median"]
+    tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+    res["prefill_4096x7168x7168_block32"] = {"gemm_us": round(us, 2), "TFLOP/s": round(tf, 1),
+                                             "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+    # the float32-scale kernel on the same shape and block size
+    As32 = torch.empty((M, K // 32), dtype=torch.float32, device=dev)
+    q8.quant_8bit(x, aq, As32, 32, EPS, -448.0, 448.0, True)
+    W32, Ws32 = synth.fp8_block_weights(N, K, 32, 32, seed=0)
+    W32, Ws32 = W32.to(dev), Ws32.to(dev)
+    t = KernelTimer(torch)
+    for i in range(max(reps // 2, 5) + 3):
+        with (t if i >= 3 else _Null()):
+            q8.blockwise_scaled_mm(aq, W32, As32, Ws32, torch.bfloat16, block=(32, 32), out=D)
+    torch.cuda.synchronize()
+    us32 = t.us()["median"]
+    res["prefill_4096x7168x7168_block32_float32_scales"] = {
+        "gemm_us": round(us32, 2), "TFLOP/s": round(2.0 * M * N * K / (us32 * 1e-6) / 1e12, 1)}
+    del x, aq, asb, D, W32, Ws32, As32, Wq, Wsb
+    N, K = 4096, 7168
+    copies = max(2, -(-(MALL_BYTES + (64 << 20)) // (N * K)))
+    W0, Ws0 = synth.fp8_block_weights_e8m0(N, K, 32, 32, seed=0)
+    Wl = [W0.to(dev) for _ in range(copies)]
+    Wsl = [Ws0.to(dev) for _ in range(copies)]
+    dec = {}
+    for Md in (1, 4, 16, 64):
+        xd = synth.activations(Md, K, "bf16", outlier_frac=0.01, seed=0).to(dev)
+        aqd = torch.empty((Md, K), dtype=torch.float8_e4m3fn, device=dev)
+        asd = torch.empty((Md, K // 32), dtype=torch.uint8, device=dev)
+        q8.quant_8bit(xd, aqd, asd, 32, EPS, -448.0, 448.0, 2)
+        Dd = torch.empty((Md, N), dtype=torch.bfloat16, device=dev)
+        g = batched_us(torch, lambda c: q8.blockwise_scaled_mm_e8m0(aqd, Wl[c], asd, Wsl[c], block_n=32,
+                                                                      out=Dd), copies, 30)
+        nbytes = N * K + Ws0.numel() + Md * K + Md * (K // 32) + Md * N * 2
+        gbs = nbytes / (g["median"] * 1e-6) / 1e9
+        dec[f"M{Md}"] = {"gemm_us": round(g["median"], 3), "algorithmic_bytes": nbytes,
+                         "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    res["decode_4096x7168_block32"] = dec
+    return res
+
+
 def bench_int8(torch, q8, synth, reps):
     M, N, K = 2048, 8192, 8192
     dev = "cuda:0"
@@ -488,6 +548,8 @@ def main() -> int:
         log(f"quant: {json.dumps(paths['quant_4096x7168'])}")
         paths["silu_quant"] = bench_silu_quant(torch, q8, synth, 30)
         log(f"silu quant: {json.dumps(paths['silu_quant'])}")
+        paths["e8m0_block32"] = bench_e8m0(torch, q8, synth, reps)
+        log(f"e8m0: {json.dumps(paths['e8m0_block32'])}")
         paths["int8_2048x8192x8192"] = bench_int8(torch, q8, synth, reps)
         log(f"int8: {json.dumps(paths['int8_2048x8192x8192'])}")
         paths["fp8_per_token_x_channel_4096x7168x7168"] = bench_fp8_scaled(torch, q8, synth, reps)

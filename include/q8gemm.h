@@ -82,6 +82,11 @@ const char* q8gemm_last_error(void);
  * group_size must divide K (PER_GROUP); it is ignored by the other modes.
  * eps > 0 floors a (an all-zero group gets s = eps/qmax and zero codes).
  * Typical ranges: FP8 qmin=-448, qmax=448; INT8 qmin=-128, qmax=127.
+ * scale_ue8m0: 0 plain float32 scales; 1 UE8M0-rounded scales stored as
+ * float32; 2 UE8M0-rounded scales stored packed as their E8M0 byte (the
+ * biased exponent b, s = 2^(b - 127); the float8_e8m0fnu scale dtype of the
+ * vLLM scaled_mm page), s then being a uint8 buffer of the same shape
+ * ([M, K/group_size] or [1]) passed through this float* argument.
  * scale_ue8m0 must be 0 with Q8_SCALE_STATIC.
  *
  * Fused SiLU-and-mul and masked rows (the same page names a second version of
@@ -138,6 +143,32 @@ int blockwise_scaled_mm(const void* A, const float* As, const void* W, const flo
                         const void* bias, void* D, q8_dtype out_dtype,
                         int64_t M, int64_t N, int64_t K, int bn, int bk,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Block-scaled FP8 GEMM with power-of-two (E8M0) block scales on both
+ * operands, applied by the matrix cores (gfx950 MX-scaled MFMA).
+ * The block32 DeepGEMM PR for DeepSeek-V4.1 ("[SM90] Use native block32
+ * DeepGEMM for DeepSeek-V4.1"), Modifications: recipe (1, bn, 32) with UE8M0
+ * activation scales; vLLM scaled_mm page (XPUFp8BlockScaledMMKernel): weight
+ * scales stored as float8_e8m0fnu bytes. A byte b is the scale 2^(b - 127).
+ *
+ *   D[m,n] = sum_kb 2^(As[m,kb]-127) * 2^(Ws[n/bn,kb]-127)
+ *            * sum_{k in kb} A[m,k] * W[n,k]   (+ bias[n]), RNE to out_dtype
+ *
+ * over 32-wide K blocks kb.
+ * A   [M, K] e4m3fn, As [M, K/32] uint8 E8M0 (quant_8bit with
+ *     scale_ue8m0 = 2 and group_size 32 writes this).
+ * W   [N, K] e4m3fn, Ws [ceil(N/bn), K/32] uint8 E8M0.
+ * bias [N] of out_dtype, or NULL.   D [M, N] of out_dtype (Q8_BF16, Q8_F16).
+ * Rules: K a positive multiple of 128; bn a positive multiple of 16; any
+ * M >= 0, N >= 1; As and Ws 4-byte aligned; A and W each below 4 GiB.
+ * Byte 255 (NaN) is not a valid scale (documented, not checked).
+ * Accumulation: FP8 products scaled and summed in float32 inside the matrix
+ * cores (order unspecified). Caller owns all buffers; asynchronous on stream.
+ */
+int blockwise_scaled_mm_e8m0(const void* A, const uint8_t* As, const void* W, const uint8_t* Ws,
+                             const void* bias, void* D, q8_dtype out_dtype,
+                             int64_t M, int64_t N, int64_t K, int bn, hipStream_t stream);
 
 /*
  * INT8 W8A8 scaled GEMM.

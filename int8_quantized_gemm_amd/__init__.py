@@ -40,6 +40,7 @@ EXPORTS = (
     "q8gemm_last_error",
     "quant_8bit_workspace_size", "quant_8bit",
     "blockwise_scaled_mm_workspace_size", "blockwise_scaled_mm",
+    "blockwise_scaled_mm_e8m0",
     "scaled_mm_int8",
     "scaled_mm_fp8",
     "moe_finalize",
@@ -65,6 +66,7 @@ _quant = _sig("quant_8bit", _i, _p, _i, _i64, _i64, _i64, _p, _i, _p, _i64, _i, 
 _bmm_ws = _sig("blockwise_scaled_mm_workspace_size", _sz, _i64, _i64, _i64, _i, _i)
 _bmm = _sig("blockwise_scaled_mm", _i, _p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i, _i, _p,
             _sz, _p)
+_bmm8 = _sig("blockwise_scaled_mm_e8m0", _i, _p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i, _p)
 _imm = _sig("scaled_mm_int8", _i, _p, _p, _i64, _p, _p, _i64, _p, _p, _i, _i64, _i64, _i64, _p)
 _fin = _sig("moe_finalize", _i, _p, _i, _p, _p, _i64, _i, _i64, _p, _p)
 _fmm = _sig("scaled_mm_fp8", _i, _p, _p, _i64, _p, _p, _i64, _p, _p, _i, _i64, _i64, _i64, _p)
@@ -159,7 +161,8 @@ def quant_8bit(input: torch.Tensor, output_q: torch.Tensor, output_s: torch.Tens
     ``input`` [M, K] (fp32/bf16/f16, unit column stride), ``output_q`` [M, K]
     float8_e4m3fn/uint8 codes or int8, ``output_s`` [M, K // group_size]
     float32 (``[1]`` for the per-tensor modes; an input for SCALE_STATIC).
-    For INT8 pass ``fp8_min=-128, fp8_max=127``.
+    For INT8 pass ``fp8_min=-128, fp8_max=127``. ``scale_ue8m0=2`` stores the
+    UE8M0 scales as their E8M0 bytes (``output_s`` uint8).
 
     ``fuse_silu_and_mul``: ``input`` is [..., 2K] (rows [gate | up]) and the
     codes are of ``silu(gate) * up``. ``masked_m`` (int32 [E]): ``input`` is
@@ -214,6 +217,30 @@ def blockwise_scaled_mm(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torc
     ws, wsb = _workspace(dev, _bmm_ws(M, N, K, bn, bk))
     _check(_bmm(_ptr(mat_a), _ptr(scales_a), _ptr(mat_b), _ptr(scales_b), _ptr(bias), _ptr(out),
                 _dt(out.dtype), M, N, K, bn, bk, ws, wsb, _stream(dev)))
+    return out
+
+
+def blockwise_scaled_mm_e8m0(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torch.Tensor,
+                             scales_b: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                             bias: torch.Tensor | None = None, block_n: int = 32,
+                             out: torch.Tensor | None = None) -> torch.Tensor:
+    """Block-scaled FP8 GEMM with E8M0 (power-of-two) scales on both operands:
+    ``scales_a`` [M, K/32] and ``scales_b`` [ceil(N/block_n), K/32] as uint8
+    (or torch.float8_e8m0fnu) bytes, 32-wide K blocks."""
+    dev = _dev(mat_a, mat_b, scales_a, scales_b, bias, out)
+    _contig(mat_a, mat_b, scales_a, scales_b, bias)
+    M, K = mat_a.shape
+    N = mat_b.shape[0]
+    if mat_b.shape[1] != K:
+        raise ValueError("mat_b must be [N, K]")
+    for t in (scales_a, scales_b):
+        if t.element_size() != 1:
+            raise ValueError("E8M0 scales are one byte each")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    _contig(out)
+    _check(_bmm8(_ptr(mat_a), _ptr(scales_a), _ptr(mat_b), _ptr(scales_b), _ptr(bias), _ptr(out),
+                 _dt(out.dtype), M, N, K, block_n, _stream(dev)))
     return out
 
 

@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libq8gemm.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["capi.cpp", "quant.hip", "gemm_block.hip", "gemm_scaled.hip", "moe.hip"]
+SOURCES = ["capi.cpp", "quant.hip", "gemm_block.hip", "gemm_mx.hip", "gemm_scaled.hip", "moe.hip"]
 ARCH = "gfx950"
 
 

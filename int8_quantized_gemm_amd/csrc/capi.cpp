@@ -95,6 +95,8 @@ int quant_8bit(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, int64_t ld
   if (q_dtype == Q8_I8 && (qmax > 127.0f || qmin < -128.0f))
     return fail(Q8_EINVAL, "%s: INT8 clip range must lie within [-128, 127]", fn);
   if (mode != Q8_SCALE_STATIC && !(eps > 0.0f)) return fail(Q8_EINVAL, "%s: eps must be > 0", fn);
+  if (scale_ue8m0 < 0 || scale_ue8m0 > 2)
+    return fail(Q8_EINVAL, "%s: scale_ue8m0 must be 0, 1 or 2", fn);
   if (mode == Q8_SCALE_STATIC && scale_ue8m0)
     return fail(Q8_EINVAL, "%s: scale_ue8m0 applies to computed scales, not a static scale", fn);
   if (mode == Q8_SCALE_PER_GROUP) {
@@ -133,6 +135,27 @@ int blockwise_scaled_mm(const void* A, const float* As, const void* W, const flo
   a.bias = bias; a.D = D; a.out_dtype = out_dtype;
   a.M = M; a.N = N; a.K = K; a.bn = bn; a.bk = bk;
   return hip_status(q8::launch_blockwise(a, stream), fn);
+}
+
+int blockwise_scaled_mm_e8m0(const void* A, const uint8_t* As, const void* W, const uint8_t* Ws,
+                             const void* bias, void* D, q8_dtype out_dtype, int64_t M, int64_t N,
+                             int64_t K, int bn, hipStream_t stream) {
+  static const char* fn = "blockwise_scaled_mm_e8m0";
+  if (!is_16bit_out(out_dtype)) return fail(Q8_EINVAL, "%s: out_dtype must be BF16 or F16", fn);
+  if (M < 0 || N < 1 || K < 1) return fail(Q8_ESHAPE, "%s: need M >= 0, N >= 1, K >= 1", fn);
+  if (bn < 16 || bn % 16 != 0)
+    return fail(Q8_EUNSUPPORTED, "%s: bn must be a positive multiple of 16 (got %d)", fn, bn);
+  if (K % 128 != 0)
+    return fail(Q8_ESHAPE, "%s: K (%lld) must be a multiple of 128", fn, (long long)K);
+  if (M * K >= (int64_t)1 << 32 || N * K >= (int64_t)1 << 32)
+    return fail(Q8_EUNSUPPORTED, "%s: A and W must each be below 4 GiB", fn);
+  if (M == 0) return ok();
+  if (!A || !As || !W || !Ws || !D) return fail(Q8_EINVAL, "%s: null pointer", fn);
+  if ((uintptr_t)As % 4 != 0 || (uintptr_t)Ws % 4 != 0)
+    return fail(Q8_EINVAL, "%s: As and Ws must be 4-byte aligned", fn);
+  q8::MxGemmArgs a{static_cast<const uint8_t*>(A), As, static_cast<const uint8_t*>(W), Ws,
+                   bias, D, out_dtype, M, N, K, bn};
+  return hip_status(q8::launch_blockwise_e8m0(a, stream), fn);
 }
 
 int scaled_mm_int8(const int8_t* A, const float* sa, int64_t sa_numel, const int8_t* W,

@@ -1,0 +1,377 @@
+// Block-scaled FP8 GEMM with power-of-two (E8M0) block scales on both
+// operands, applied by gfx950's MX-scaled matrix instruction.
+//
+// The block32 DeepGEMM PR for DeepSeek-V4.1 ("[SM90] Use native block32
+// DeepGEMM for DeepSeek-V4.1"): recipe (1, bn, 32) with UE8M0 activation
+// scales; the vLLM scaled_mm page (XPUFp8BlockScaledMMKernel): weight scales
+// stored as float8_e8m0fnu bytes. An E8M0 byte b is the scale 2^(b - 127):
+//
+//   D[m,n] = sum_kb 2^(As[m,kb]-127) 2^(Ws[n/bn,kb]-127) sum_{k in kb} A[m,k] W[n,k]
+//
+// over 32-wide K blocks kb (+ bias[n], then RNE to bf16/f16).
+//
+// v_mfma_scale_f32_16x16x128_f8f6f4 takes one E8M0 byte per lane for each
+// operand. In its K numbering (measured on gfx950 with single non-zero
+// registers) lane group g = l / 16 holds K elements [16g, 16g + 16) in its
+// first four registers and [64 + 16g, 64 + 16g + 16) in its last four, for
+// row l % 16; the scale of 32-wide block kb (K elements [32kb, 32kb + 32)) of
+// row r is the byte supplied by lane r + 16 kb. With the K bytes of a
+// 128-byte slab laid out that way, the block scales are applied inside the
+// matrix core and the K loop accumulates in the MFMA accumulators: no VALU
+// work per K block, unlike the float32-scale kernel, which adds every block's
+// partial product with an FMA.
+//
+// gemm_tile_mx   (M > 64) 256 x 256 output tiles, 128-byte K slabs
+//                double-buffered in LDS through direct buffer -> LDS loads, as
+//                the float32-scale tile kernel, whose fragment (16-byte chunks
+//                g and g + 4 of the slab for lane group g) is already that
+//                layout. Scale dwords (four blocks of one row) are loaded from
+//                global memory one slab ahead.
+// gemm_stream_mx (M <= 64) streams W once, one workgroup per 16 weight rows,
+//                lane group g loading bytes [16g, 16g + 16) and
+//                [64 + 16g, 64 + 16g + 16) of each 128-byte chunk.
+#include "q8_internal.h"
+#include "tile_common.h"
+
+namespace q8 {
+namespace {
+
+struct MxParams {
+  const uint8_t* A;
+  const uint8_t* As;
+  const uint8_t* W;
+  const uint8_t* Ws;
+  const void* bias;
+  void* D;
+  int64_t M, N, K;
+  int KB;   // K / 32: bytes per scale row
+  int bn;
+  int nbw;  // ceil(N / bn)
+  int out_bf16;
+  int d_vec4;
+  uint32_t a_bytes, as_bytes;
+  int64_t tiles_m, tiles_n;
+};
+
+__device__ __forceinline__ f32x4 mfma_mx(const i32x8& w, const i32x8& a, const f32x4& c,
+                                         uint32_t sw, uint32_t sa) {
+  // operand 0 = weight rows, operand 1 = activation rows, both FP8 e4m3
+  // (format codes 0); byte 0 of each scale register is used
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, a, c, 0, 0, 0, (int)sw, 0, (int)sa);
+}
+
+__device__ __forceinline__ i32x8 lds_frag_mx(const uint8_t* base, int row, int g) {
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(base + swz(row, g));
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(base + swz(row, g + 4));
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Fragment of lane group g from global memory: p points at byte 16g of a
+// 128-byte chunk; bytes [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16).
+__device__ __forceinline__ i32x8 gload_mx(const uint8_t* p) {
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 64);
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ uint32_t out_bits(float v, bool bf16) {
+  return bf16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
+}
+
+__device__ __forceinline__ float bias_at(const void* b, int64_t n, bool bf16) {
+  const uint16_t h = static_cast<const uint16_t*>(b)[n];
+  return bf16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+}
+
+// D[row, n .. n+3] (+ bias) as 16-bit values
+__device__ __forceinline__ void store4_mx(const MxParams& p, int64_t row, int64_t n, f32x4 v,
+                                          bool bf16, bool vec) {
+  uint16_t* D = static_cast<uint16_t*>(p.D);
+  const int64_t N = p.N;
+  if (vec && n + 3 < N) {
+    if (p.bias) {
+      const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.bias) + n);
+      const uint32_t h[4] = {b.x & 0xFFFFu, b.x >> 16, b.y & 0xFFFFu, b.y >> 16};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] += bf16 ? bf16_bits_to_f32(h[r]) : f16_bits_to_f32(h[r]);
+    }
+    uint2 o;
+    o.x = out_bits(v[0], bf16) | (out_bits(v[1], bf16) << 16);
+    o.y = out_bits(v[2], bf16) | (out_bits(v[3], bf16) << 16);
+    *reinterpret_cast<uint2*>(D + row * N + n) = o;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (n + r >= N) break;
+      const float bv = p.bias ? bias_at(p.bias, n + r, bf16) : 0.0f;
+      D[row * N + n + r] = (uint16_t)out_bits(v[r] + bv, bf16);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_tile_mx(MxParams p) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int A_SLOTS = BM / 8, B_SLOTS = BN / 8;  // 1 KB (8 rows) per wave load
+  constexpr int A_PER = (A_SLOTS + NW - 1) / NW, B_PER = (B_SLOTS + NW - 1) / NW;
+  static_assert(TM % 16 == 0 && TN % 16 == 0 && NW % 2 == 0, "tile");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * 128];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w / WN, wn = w % WN;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t M = p.M, N = p.N, K = p.K;
+  const int KB = p.KB;
+
+  const int64_t t = xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n);
+  int64_t tm, tn;
+  grouped_order(t, p.tiles_m, p.tiles_n, 8, tm, tn);
+  const int64_t m_lo = tm * BM, n0 = tn * BN;
+
+  // Wave load q fills rows 8q..8q+7 of a stage; lane l writes physical chunk
+  // l % 8 of row 8q + l / 8, which holds chunk c = (l % 8) ^ key of the row's
+  // slab, key = swz_key(row) = (4q + l / 16) % 8 (the wave's parity fixes q's).
+  const int key = (4 * (w & 1) + (lane >> 4)) & 7;
+  const uint32_t lane_off = (uint32_t)((lane >> 3) * K + (((lane & 7) ^ key) << 4));
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, p.a_bytes);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.W, (uint32_t)(N * K));
+  const uint32_t a_base = (uint32_t)(m_lo * K), b_base = (uint32_t)(n0 * K);
+  auto issue = [&](int kt, uint8_t* __restrict__ la, uint8_t* __restrict__ lb) {
+#pragma unroll
+    for (int c = 0; c < A_PER; ++c) {
+      const int q = w + c * NW;
+      if (A_SLOTS % NW == 0 || q < A_SLOTS)
+        b2l16(rA, lane_off, a_base + (uint32_t)(8 * q) * (uint32_t)K + kt * 128, la + q * 1024);
+    }
+#pragma unroll
+    for (int c = 0; c < B_PER; ++c) {
+      const int q = w + c * NW;
+      if (B_SLOTS % NW == 0 || q < B_SLOTS)
+        b2l16(rB, lane_off, b_base + (uint32_t)(8 * q) * (uint32_t)K + kt * 128, lb + q * 1024);
+    }
+  };
+
+  // Scale dwords (the four 32-wide blocks of a slab for one row) are staged
+  // in LDS with the slab, one 4-byte buffer -> LDS load per wave: waves
+  // 0..NW/2-1 fetch activation rows, the others weight rows. Table layouts
+  // follow the lanes that read them: activation position (wm*16 + r16)*FM + i
+  // holds row wm*TM + i*16 + r16, weight position (wn*16 + r16)*FN + j holds
+  // row wn*TN + j*16 + r16, so a lane reads its FM (FN) dwords contiguously.
+  // Rows past the end of As / Ws read as zero (their outputs are never stored).
+  static_assert(WM * 16 * FM == BM && WN * 16 * FN == BN && BM == BN && BM == NW / 2 * 64,
+                "one scale load per wave covers the tile's rows");
+  __shared__ __attribute__((aligned(16))) uint32_t sSA[2][BM];
+  __shared__ __attribute__((aligned(16))) uint32_t sSW[2][BN];
+  const __amdgpu_buffer_rsrc_t rAs = make_rsrc(p.As, p.as_bytes);
+  const __amdgpu_buffer_rsrc_t rWs = make_rsrc(p.Ws, (uint32_t)(p.nbw * KB));
+  const bool a_side = w < NW / 2;
+  const int pos0 = (a_side ? w : w - NW / 2) * 64;
+  uint32_t vo_s;
+  if (a_side) {
+    const int pos = pos0 + lane;
+    const int wm_ = pos / (16 * FM), r_ = (pos / FM) % 16, i_ = pos % FM;
+    vo_s = (uint32_t)((m_lo + wm_ * TM + i_ * 16 + r_) * KB);
+  } else {
+    const int pos = pos0 + lane;
+    const int wn_ = pos / (16 * FN), r_ = (pos / FN) % 16, j_ = pos % FN;
+    const int64_t n = n0 + wn_ * TN + j_ * 16 + r_;
+    vo_s = (uint32_t)((n < N ? n / p.bn : (int64_t)p.nbw) * KB);
+  }
+  auto issue_scales = [&](int kt, int stage) {
+    if (a_side) b2l4(rAs, vo_s, 4 * kt, &sSA[stage][pos0]);
+    else b2l4(rWs, vo_s, 4 * kt, &sSW[stage][pos0]);
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](int kt, bool refill, uint8_t* __restrict__ na, uint8_t* __restrict__ nb,
+                  const uint8_t* __restrict__ la, const uint8_t* __restrict__ lb) {
+    const int st = kt & 1;
+    if (refill) {
+      issue(kt + 1, na, nb);
+      issue_scales(kt + 1, st ^ 1);
+    }
+    // this slab's scale bytes for lane group g (block 4 kt + g), shifted to byte 0
+    uint32_t sa[FM], sw[FN];
+#pragma unroll
+    for (int i4 = 0; i4 < FM / 4; ++i4) {
+      const i32x4 v = *reinterpret_cast<const i32x4*>(&sSA[st][(wm * 16 + r16) * FM + 4 * i4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sa[4 * i4 + e] = (uint32_t)v[e] >> (8 * g);
+    }
+#pragma unroll
+    for (int j4 = 0; j4 < FN / 4; ++j4) {
+      const i32x4 v = *reinterpret_cast<const i32x4*>(&sSW[st][(wn * 16 + r16) * FN + 4 * j4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sw[4 * j4 + e] = (uint32_t)v[e] >> (8 * g);
+    }
+    i32x8 bw[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bw[j] = lds_frag_mx(lb, wn * TN + j * 16 + r16, g);
+    i32x8 av[2];
+    av[0] = lds_frag_mx(la, wm * TM + r16, g);
+    // the wave ahead yields to the one behind halfway through the slab (see
+    // the float32-scale tile kernel)
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (i == FM / 2) __builtin_amdgcn_s_setprio(0);
+      if (i + 1 < FM) av[(i + 1) & 1] = lds_frag_mx(la, wm * TM + (i + 1) * 16 + r16, g);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma_mx(bw[j], av[i & 1], acc[i][j], sw[j], sa[i]);
+    }
+  };
+
+  const int KT = (int)(K / 128);
+  issue(0, sA0, sB0);
+  issue_scales(0, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_vmem();
+    __syncthreads();
+    const bool odd = kt & 1;
+    step(kt, kt + 1 < KT, odd ? sA0 : sA1, odd ? sB0 : sB1, odd ? sA1 : sA0, odd ? sB1 : sB0);
+  }
+
+  const bool bf16 = p.out_bf16 != 0, vec = p.d_vec4 != 0;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t row = m_lo + wm * TM + i * 16 + r16;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = n0 + wn * TN + j * 16 + 4 * g;
+      if (n >= N) continue;
+      store4_mx(p, row, n, acc[i][j], bf16, vec);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------
+// One workgroup per 16 weight rows (x a 16*MT-row activation block); its NW
+// waves split the 128-byte K chunks, issue a round of R chunks' loads, then
+// one scaled MFMA per chunk and activation block; float32 partials of the
+// waves are summed through LDS in a fixed order (deterministic).
+template <int MT, int NW, int R>
+__global__ __launch_bounds__(NW * 64) void gemm_stream_mx(MxParams p) {
+  __shared__ f32x4 red[NW][MT][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t N = p.N, K = p.K, M = p.M;
+  const int KB = p.KB;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t m_base = (int64_t)blockIdx.y * (MT * 16);
+  const int NC = (int)(K / 128);
+  const int c_b = (int)((int64_t)w * NC / NW), c_e = (int)((int64_t)(w + 1) * NC / NW);
+
+  const int64_t nrow = n0 + r16 < N ? n0 + r16 : N - 1;
+  const uint8_t* wp = p.W + nrow * K + 16 * g;
+  const uint32_t* wsr = reinterpret_cast<const uint32_t*>(p.Ws + (nrow / p.bn) * KB);
+  const uint8_t* ap[MT];
+  const uint32_t* asr[MT];
+#pragma unroll
+  for (int mb = 0; mb < MT; ++mb) {
+    const int64_t m = m_base + mb * 16 + r16 < M ? m_base + mb * 16 + r16 : M - 1;
+    ap[mb] = p.A + m * K + 16 * g;
+    asr[mb] = reinterpret_cast<const uint32_t*>(p.As + m * KB);
+  }
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mb = 0; mb < MT; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = c_b; c0 < c_e; c0 += R) {
+    i32x8 wf[R], af[R][MT];
+    uint32_t sw[R], sa[R][MT];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int c = c0 + u < c_e ? c0 + u : c_e - 1;
+      wf[u] = gload_mx(wp + (int64_t)c * 128);
+      sw[u] = wsr[c];
+#pragma unroll
+      for (int mb = 0; mb < MT; ++mb) {
+        af[u][mb] = gload_mx(ap[mb] + (int64_t)c * 128);
+        sa[u][mb] = asr[mb][c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      if (c0 + u >= c_e) break;
+#pragma unroll
+      for (int mb = 0; mb < MT; ++mb)
+        acc[mb] = mfma_mx(wf[u], af[u][mb], acc[mb], sw[u] >> (8 * g), sa[u][mb] >> (8 * g));
+    }
+  }
+
+#pragma unroll
+  for (int mb = 0; mb < MT; ++mb) red[w][mb][lane] = acc[mb];
+  __syncthreads();
+  const bool bf16 = p.out_bf16 != 0, vec = p.d_vec4 != 0;
+  for (int idx = tid; idx < MT * 64; idx += NW * 64) {
+    const int mb = idx >> 6, l2 = idx & 63;
+    const int64_t m = m_base + mb * 16 + (l2 & 15);
+    if (m >= M) continue;
+    f32x4 sum = red[0][mb][l2];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) sum += red[ww][mb][l2];
+    const int64_t n = n0 + 4 * (l2 >> 4);
+    if (n < N) store4_mx(p, m, n, sum, bf16, vec);
+  }
+}
+
+constexpr int kMxBM = 256, kMxBN = 256, kMxWM = 2, kMxWN = 4;
+constexpr int kMxStreamNW = 16;
+
+template <int MT>
+hipError_t launch_stream_mx(const MxParams& p, hipStream_t st) {
+  const dim3 grid((unsigned)((p.N + 15) / 16), (unsigned)((p.M + MT * 16 - 1) / (MT * 16)));
+  constexpr int R = MT == 1 ? 4 : 2;
+  hipLaunchKernelGGL((gemm_stream_mx<MT, kMxStreamNW, R>), grid, dim3(kMxStreamNW * 64), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_blockwise_e8m0(const MxGemmArgs& a, hipStream_t st) {
+  if (a.M == 0) return hipSuccess;
+  MxParams p{};
+  p.A = a.A; p.As = a.As; p.W = a.W; p.Ws = a.Ws; p.bias = a.bias; p.D = a.D;
+  p.M = a.M; p.N = a.N; p.K = a.K;
+  p.KB = (int)(a.K / 32);
+  p.bn = a.bn;
+  p.nbw = (int)((a.N + a.bn - 1) / a.bn);
+  p.out_bf16 = a.out_dtype == Q8_BF16;
+  p.d_vec4 = a.N % 4 == 0 && (uintptr_t)a.D % 8 == 0 && (uintptr_t)a.bias % 8 == 0;
+  p.a_bytes = (uint32_t)(a.M * a.K);
+  p.as_bytes = (uint32_t)(a.M * (a.K / 32));
+  p.tiles_m = (a.M + kMxBM - 1) / kMxBM;
+  p.tiles_n = (a.N + kMxBN - 1) / kMxBN;
+  if (a.M <= 64) {
+    const int mt = (int)((a.M + 15) / 16);
+    switch (mt) {
+      case 1: return launch_stream_mx<1>(p, st);
+      case 2: return launch_stream_mx<2>(p, st);
+      case 3: return launch_stream_mx<3>(p, st);
+      default: return launch_stream_mx<4>(p, st);
+    }
+  }
+  const int64_t tiles = p.tiles_m * p.tiles_n;
+  if (tiles > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((gemm_tile_mx<kMxBM, kMxBN, kMxWM, kMxWN>), dim3((unsigned)tiles),
+                     dim3(kMxWM * kMxWN * 64), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace q8

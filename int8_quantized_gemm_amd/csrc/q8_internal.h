@@ -40,6 +40,14 @@ hipError_t launch_blockwise(const BlockGemmArgs& a, hipStream_t stream);
 hipError_t launch_grouped(const BlockGemmArgs& a, int64_t total_m, int32_t* c_inv_ws,
                           const int32_t* c_map, hipStream_t stream);
 
+// ---- block-scaled FP8 GEMM, E8M0 scales (MX-scaled MFMA) ---------------------
+struct MxGemmArgs {
+  const uint8_t* A; const uint8_t* As; const uint8_t* W; const uint8_t* Ws;
+  const void* bias; void* D; q8_dtype out_dtype;
+  int64_t M, N, K; int bn;
+};
+hipError_t launch_blockwise_e8m0(const MxGemmArgs& a, hipStream_t stream);
+
 // ---- INT8 GEMM ----------------------------------------------------------------
 struct ScaledGemmArgs {
   const void* A; const float* sa; int64_t sa_numel;

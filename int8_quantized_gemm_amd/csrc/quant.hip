@@ -135,6 +135,14 @@ struct Divider {
   }
 };
 
+// Scale store: UE = 2 keeps a UE8M0 scale as its E8M0 byte (the biased
+// exponent; s = 2^(b - 127)), in a uint8 [M, K/g] buffer; otherwise float32.
+template <int UE>
+__device__ __forceinline__ void store_scale(float* s, int64_t i, float sc) {
+  if constexpr (UE == 2) reinterpret_cast<uint8_t*>(s)[i] = (uint8_t)(__float_as_uint(sc) >> 23);
+  else s[i] = sc;
+}
+
 template <bool FP8>
 __device__ __forceinline__ uint32_t encode_pair_bytes(float a, float b) {
   if constexpr (FP8) {
@@ -183,7 +191,7 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 #endif
 constexpr int kUnroll8 = Q8_QUANT_UNROLL8;
 
-template <int XT, bool FP8, bool UE, int TPG, bool CONTIG, int EPL>
+template <int XT, bool FP8, int UE, int TPG, bool CONTIG, int EPL>
 __global__ __launch_bounds__(kThreads) void quant_group_wave(
     const void* __restrict__ x, int64_t M, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
     float* __restrict__ s, float eps, float qmin, float qmax) {
@@ -222,9 +230,9 @@ __global__ __launch_bounds__(kThreads) void quant_group_wave(
 #pragma unroll
       for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[u][h][i]));
     a = wave_max_xor(a, TPG);
-    const float sc = group_scale<UE>(a, eps, qmax);
+    const float sc = group_scale<(UE != 0)>(a, eps, qmax);
     if (v >= total) continue;
-    const Divider<UE> div(sc);
+    const Divider<(UE != 0)> div(sc);
     // the output is contiguous in either case: vector v is bytes [EPL v,
     // EPL v + EPL) of q and group v / TPG of s
     if constexpr (EPL == 8) {
@@ -238,11 +246,11 @@ __global__ __launch_bounds__(kThreads) void quant_group_wave(
       const uint2 lo = encode8<FP8>(y0), hi = encode8<FP8>(y1);
       *reinterpret_cast<uint4*>(q + (int64_t)v * 16) = uint4{lo.x, lo.y, hi.x, hi.y};
     }
-    if ((v & (TPG - 1)) == 0) s[v / TPG] = sc;
+    if ((v & (TPG - 1)) == 0) store_scale<UE>(s, v / TPG, sc);
   }
 }
 
-template <int XT, bool FP8, bool UE, bool VEC>
+template <int XT, bool FP8, int UE, bool VEC>
 __global__ __launch_bounds__(kThreads) void quant_group_block(
     const void* __restrict__ x, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
     float* __restrict__ s, int64_t g, float eps, float qmin, float qmax) {
@@ -264,9 +272,9 @@ __global__ __launch_bounds__(kThreads) void quant_group_block(
     for (int64_t i = threadIdx.x; i < g; i += kThreads) a = fmaxf(a, fabsf(load1<XT>(x, xb + i)));
   }
   a = block_max(a, red);
-  const float sc = group_scale<UE>(a, eps, qmax);
-  if (threadIdx.x == 0) s[blockIdx.x] = sc;
-  const Divider<UE> div(sc);
+  const float sc = group_scale<(UE != 0)>(a, eps, qmax);
+  if (threadIdx.x == 0) store_scale<UE>(s, blockIdx.x, sc);
+  const Divider<(UE != 0)> div(sc);
   if constexpr (VEC) {
     for (int64_t i = (int64_t)threadIdx.x * 8; i < g; i += kThreads * 8) {
       float f[8], y[8];
@@ -284,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void quant_group_block(
 // One workgroup per group of up to kThreads * 8 * NV elements (a per-token
 // row, say) held in registers: one read of the input, a block reduction, then
 // the codes, instead of re-reading the group after the reduction.
-template <int XT, bool FP8, bool UE, int NV>
+template <int XT, bool FP8, int UE, int NV>
 __global__ __launch_bounds__(kThreads) void quant_group_regs(
     const void* __restrict__ x, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
     float* __restrict__ s, int64_t g, float eps, float qmin, float qmax) {
@@ -306,9 +314,9 @@ __global__ __launch_bounds__(kThreads) void quant_group_regs(
     }
   }
   a = block_max(a, red);
-  const float sc = group_scale<UE>(a, eps, qmax);
-  if (threadIdx.x == 0) s[blockIdx.x] = sc;
-  const Divider<UE> div(sc);
+  const float sc = group_scale<(UE != 0)>(a, eps, qmax);
+  if (threadIdx.x == 0) store_scale<UE>(s, blockIdx.x, sc);
+  const Divider<(UE != 0)> div(sc);
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int64_t i = ((int64_t)v * kThreads + threadIdx.x) * 8;
@@ -347,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void amax_partials(const void* __restrict
   if (threadIdx.x == 0) partial[blockIdx.x] = a;
 }
 
-template <int XT, bool FP8, bool UE, bool VEC, bool STATIC>
+template <int XT, bool FP8, int UE, bool VEC, bool STATIC>
 __global__ __launch_bounds__(kThreads) void quant_tensor(
     const void* __restrict__ x, int64_t M, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
     float* __restrict__ s, const float* __restrict__ partial, int nparts, float eps, float qmin,
@@ -360,10 +368,10 @@ __global__ __launch_bounds__(kThreads) void quant_tensor(
     float a = 0.0f;
     for (int i = threadIdx.x; i < nparts; i += kThreads) a = fmaxf(a, partial[i]);
     a = block_max(a, red);
-    sc = group_scale<UE>(a, eps, qmax);
-    if (blockIdx.x == 0 && threadIdx.x == 0) s[0] = sc;
+    sc = group_scale<(UE != 0)>(a, eps, qmax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) store_scale<UE>(s, 0, sc);
   }
-  const Divider<UE> div(sc);
+  const Divider<(UE != 0)> div(sc);
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   if constexpr (VEC) {
     const int64_t vpr = K >> 3, total = M * vpr;
@@ -448,7 +456,7 @@ __device__ __forceinline__ bool row_live(const int32_t* __restrict__ masked_m, u
 // lanes are adjacent and reduce their |max| with xor shuffles. Rows are
 // addressed through ld_x (the input is [M, 2K] with SILU, [M, K] without),
 // the codes and scales are contiguous. The host keeps M * K / 16 below 2^32.
-template <int XT, bool FP8, bool UE, int TPG, bool SILU>
+template <int XT, bool FP8, int UE, int TPG, bool SILU>
 __global__ __launch_bounds__(kThreads) void quant_fused_wave(
     const void* __restrict__ x, int64_t M, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
     float* __restrict__ s, const int32_t* __restrict__ masked_m, uint32_t max_m, float eps,
@@ -491,19 +499,19 @@ __global__ __launch_bounds__(kThreads) void quant_fused_wave(
     for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(y[h][i]));
   a = wave_max_xor(a, TPG);  // every lane takes part; dead lanes add 0
   if (!live) return;
-  const float sc = group_scale<UE>(a, eps, qmax);
-  const Divider<UE> div(sc);
+  const float sc = group_scale<(UE != 0)>(a, eps, qmax);
+  const Divider<(UE != 0)> div(sc);
   float c0[8], c1[8];
   div.apply8(y[0], c0, qmin, qmax);
   div.apply8(y[1], c1, qmin, qmax);
   const uint2 lo = encode8<FP8>(c0), hi = encode8<FP8>(c1);
   *reinterpret_cast<uint4*>(q + (int64_t)v * 16) = uint4{lo.x, lo.y, hi.x, hi.y};
-  if ((v & (TPG - 1)) == 0) s[v / TPG] = sc;
+  if ((v & (TPG - 1)) == 0) store_scale<UE>(s, v / TPG, sc);
 }
 
 // Any group size: one workgroup per group, element-wise loads, a block
 // reduction, then a second pass that recomputes y and writes the codes.
-template <int XT, bool FP8, bool UE, bool SILU>
+template <int XT, bool FP8, int UE, bool SILU>
 __global__ __launch_bounds__(kThreads) void quant_fused_block(
     const void* __restrict__ x, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
     float* __restrict__ s, int64_t g, const int32_t* __restrict__ masked_m, uint32_t max_m,
@@ -523,13 +531,13 @@ __global__ __launch_bounds__(kThreads) void quant_fused_block(
   float a = 0.0f;
   for (int64_t i = threadIdx.x; i < g; i += kThreads) a = fmaxf(a, fabsf(value(i)));
   a = block_max(a, red);
-  const float sc = group_scale<UE>(a, eps, qmax);
-  if (threadIdx.x == 0) s[blockIdx.x] = sc;
-  const Divider<UE> div(sc);
+  const float sc = group_scale<(UE != 0)>(a, eps, qmax);
+  if (threadIdx.x == 0) store_scale<UE>(s, blockIdx.x, sc);
+  const Divider<(UE != 0)> div(sc);
   for (int64_t i = threadIdx.x; i < g; i += kThreads) q[qb + i] = encode1<FP8>(div(value(i), qmin, qmax));
 }
 
-template <int XT, bool FP8, bool UE, bool SILU>
+template <int XT, bool FP8, int UE, bool SILU>
 hipError_t dispatch_fused(const QuantArgs& a, hipStream_t st) {
   const int esz = XT == Q8_F32 ? 4 : 2;
   const int64_t g = a.group_size;
@@ -563,7 +571,7 @@ hipError_t dispatch_fused(const QuantArgs& a, hipStream_t st) {
 }
 
 // ---- host dispatch -------------------------------------------------------------
-template <int XT, bool FP8, bool UE>
+template <int XT, bool FP8, int UE>
 hipError_t dispatch(const QuantArgs& a, hipStream_t st) {
   const int esz = XT == Q8_F32 ? 4 : 2;
   const bool vec = (a.K % 8 == 0) && (a.ld_x % (esz == 2 ? 8 : 4) == 0) &&
@@ -660,19 +668,24 @@ hipError_t dispatch(const QuantArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int XT, bool FP8, bool UE>
+template <int XT, bool FP8, int UE>
 hipError_t dispatch_any(const QuantArgs& a, hipStream_t st) {
   if (a.silu) return dispatch_fused<XT, FP8, UE, true>(a, st);
   if (a.masked_m) return dispatch_fused<XT, FP8, UE, false>(a, st);
   return dispatch<XT, FP8, UE>(a, st);
 }
 
+template <int XT, bool FP8>
+hipError_t dispatch_ue(const QuantArgs& a, hipStream_t st) {
+  const int ue = a.mode == Q8_SCALE_STATIC ? 0 : a.ue8m0;
+  if (ue == 2) return dispatch_any<XT, FP8, 2>(a, st);
+  if (ue == 1) return dispatch_any<XT, FP8, 1>(a, st);
+  return dispatch_any<XT, FP8, 0>(a, st);
+}
+
 template <int XT>
 hipError_t dispatch_q(const QuantArgs& a, hipStream_t st) {
-  const bool ue = a.ue8m0 != 0 && a.mode != Q8_SCALE_STATIC;
-  if (a.q_dtype == Q8_E4M3FN)
-    return ue ? dispatch_any<XT, true, true>(a, st) : dispatch_any<XT, true, false>(a, st);
-  return ue ? dispatch_any<XT, false, true>(a, st) : dispatch_any<XT, false, false>(a, st);
+  return a.q_dtype == Q8_E4M3FN ? dispatch_ue<XT, true>(a, st) : dispatch_ue<XT, false>(a, st);
 }
 
 }  // namespace

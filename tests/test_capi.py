@@ -153,3 +153,27 @@ def test_moe_and_grouped_validation(q8):
     assert q8._fin(p, q8.Q8_BF16, p, p, 1 << 30, 4, 16, p, p) == q8.Q8_ESHAPE # T * topk
     assert q8._shuf(p, 16, p, 4, p, p) == q8.Q8_EINVAL
     assert q8._shuf(p, 16, p, 0, p, p) == q8.Q8_OK
+
+
+def test_e8m0_gemm_validation(q8):
+    p = None
+    args = lambda M, N, K, bn, out=q8.Q8_BF16, ptr=p: (ptr, ptr, ptr, ptr, p, ptr, out, M, N, K, bn, p)
+    assert q8._bmm8(*args(4, 256, 500, 32)) == q8.Q8_ESHAPE            # K not a multiple of 128
+    assert "multiple of 128" in q8.last_error()
+    assert q8._bmm8(*args(4, 256, 512, 24)) == q8.Q8_EUNSUPPORTED      # bn not a multiple of 16
+    assert q8._bmm8(*args(4, 256, 512, 32, q8.Q8_F32)) == q8.Q8_EINVAL  # output dtype
+    assert q8._bmm8(*args(4, 0, 512, 32)) == q8.Q8_ESHAPE              # N = 0
+    assert q8._bmm8(*args(4, 256, 512, 32)) == q8.Q8_EINVAL            # null pointers
+    assert q8._bmm8(*args(0, 256, 512, 32)) == q8.Q8_OK                # M = 0: no-op
+    # scale tables must be 4-byte aligned (the kernels read scale dwords)
+    assert q8._bmm8(16, 18, 16, 16, p, 16, q8.Q8_BF16, 4, 256, 512, 32, p) == q8.Q8_EINVAL
+    assert "aligned" in q8.last_error()
+    # A beyond 4 GiB
+    assert q8._bmm8(*args(1 << 20, 256, 1 << 12, 32)) == q8.Q8_EUNSUPPORTED
+
+
+def test_quant_scale_ue8m0_range(q8):
+    p = None
+    assert q8._quant(8, q8.Q8_BF16, 4, 128, 128, 8, q8.Q8_E4M3FN, 8, 32, 0, 1e-10, -448, 448, 3, 0, p, 0, p, 0, p) == q8.Q8_EINVAL
+    assert "scale_ue8m0" in q8.last_error()
+    assert q8._quant(p, q8.Q8_BF16, 0, 128, 128, p, q8.Q8_E4M3FN, p, 32, 0, 1e-10, -448, 448, 2, 0, p, 0, p, 0, p) == q8.Q8_OK
