@@ -537,6 +537,99 @@ __global__ __launch_bounds__(kThreads) void quant_fused_block(
   for (int64_t i = threadIdx.x; i < g; i += kThreads) q[qb + i] = encode1<FP8>(div(value(i), qmin, qmax));
 }
 
+// bf16 gates: the float32 steps of silu_mul before the multiply by up,
+// h(g) = g / (1 + exp(-g)), depend on the gate's 16 bits alone. For gates
+// with 2^-25 <= |g| < 128 (biased exponent 102..133) h is tabulated in LDS,
+// 2 signs x 32 exponents x 128 mantissas = 8192 float32, computed by each
+// workgroup with the same float64 exp and IEEE division as silu_mul. Outside
+// that range h has a closed form in the same float32 arithmetic:
+//   |g| < 2^-25: exp(-g) rounds to 1, d = 2 and h = g / 2 = g * 0.5 (exact);
+//   g >= 128:    exp(-g) < 2^-184 rounds to 0, d = 1 and h = g;
+//   g <= -128:   exp(-g) > 2^184 overflows to +inf and h = g / inf = -0.
+// Per element that leaves a table read, one multiply and the quantization.
+constexpr int kSiluThreads = 1024;
+constexpr int kSiluTable = 8192;
+constexpr uint32_t kSiluExpLo = 102, kSiluExpHi = 134;  // table exponent range [lo, hi)
+
+__device__ __forceinline__ float silu_h(float g) {
+  const float d = 1.0f + exp_rn32(-g);
+  return g / d;  // IEEE division (correctly rounded)
+}
+
+__device__ __forceinline__ float silu_h_bf16(float g, const float* __restrict__ tab) {
+  const uint32_t b = __float_as_uint(g) >> 16;  // the bf16 bits (g came from a bf16)
+  const uint32_t e = (b >> 7) & 0xFFu;
+  const uint32_t ec = e < kSiluExpLo ? kSiluExpLo : (e >= kSiluExpHi ? kSiluExpHi - 1 : e);
+  const float t = tab[((b >> 15) << 12) | ((ec - kSiluExpLo) << 7) | (b & 127u)];
+  const float big = (b >> 15) ? -0.0f : g;
+  return e < kSiluExpLo ? g * 0.5f : (e >= kSiluExpHi ? big : t);
+}
+
+// Same work split as quant_fused_wave (16 outputs per lane, a group's TPG
+// lanes adjacent in one wave), over a grid of at most two workgroups per CU
+// striding in whole workgroups, so each workgroup builds the table once
+// (two per CU measured 2 % faster than one at [4096, 2 x 7168]; two vectors
+// per thread and iteration were 15 % slower).
+template <bool FP8, int UE, int TPG>
+__global__ __launch_bounds__(kSiluThreads) void quant_silu_bf16_table(
+    const void* __restrict__ x, int64_t M, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
+    float* __restrict__ s, const int32_t* __restrict__ masked_m, uint32_t max_m, float eps,
+    float qmin, float qmax) {
+  __shared__ float tab[kSiluTable];
+  for (int i = threadIdx.x; i < kSiluTable; i += kSiluThreads) {
+    const uint32_t e = kSiluExpLo + ((uint32_t)i >> 7 & 31u);
+    const uint32_t b = ((uint32_t)i >> 12 << 15) | (e << 7) | ((uint32_t)i & 127u);
+    tab[i] = silu_h(__uint_as_float(b << 16));
+  }
+  __syncthreads();
+  const uint32_t vpr = (uint32_t)(K / 16);
+  const uint32_t total = (uint32_t)(M * vpr);
+  for (uint32_t base = blockIdx.x * kSiluThreads; base < total; base += gridDim.x * kSiluThreads) {
+    const uint32_t v = base + threadIdx.x;
+    const uint32_t vv = v < total ? v : total - 1;
+    const uint32_t row = vv / vpr;
+    const bool live = v < total && row_live(masked_m, max_m, row);
+    if (__ballot(live) == 0) continue;  // wave-uniform
+    float y[2][8];
+    if (live) {
+      const int64_t off = (int64_t)row * ld_x + (int64_t)(vv - row * vpr) * 16;
+      float u[2][8];
+      load8<Q8_BF16>(x, off, y[0]);
+      load8<Q8_BF16>(x, off + 8, y[1]);
+      load8<Q8_BF16>(x, off + K, u[0]);
+      load8<Q8_BF16>(x, off + K + 8, u[1]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[h][i] = silu_h_bf16(y[h][i], tab) * u[h][i];
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[h][i] = 0.0f;
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(y[h][i]));
+    a = wave_max_xor(a, TPG);
+    if (!live) continue;
+    const float sc = group_scale<(UE != 0)>(a, eps, qmax);
+    const Divider<(UE != 0)> div(sc);
+    float c0[8], c1[8];
+    div.apply8(y[0], c0, qmin, qmax);
+    div.apply8(y[1], c1, qmin, qmax);
+    const uint2 lo = encode8<FP8>(c0), hi = encode8<FP8>(c1);
+    *reinterpret_cast<uint4*>(q + (int64_t)v * 16) = uint4{lo.x, lo.y, hi.x, hi.y};
+    if ((v & (TPG - 1)) == 0) store_scale<UE>(s, v / TPG, sc);
+  }
+}
+
+// The table pays for itself from a few million elements on (building it costs
+// each workgroup about as much as 8192 elements of the direct evaluation).
+constexpr int64_t kSiluTableMinElems = 1 << 22;
+
 template <int XT, bool FP8, int UE, bool SILU>
 hipError_t dispatch_fused(const QuantArgs& a, hipStream_t st) {
   const int esz = XT == Q8_F32 ? 4 : 2;
@@ -548,6 +641,26 @@ hipError_t dispatch_fused(const QuantArgs& a, hipStream_t st) {
   const bool wave = g >= 16 && g <= 512 && (g & (g - 1)) == 0 && total < 0xFFFF0000LL &&
                     (uintptr_t)a.x % 16 == 0 && (uintptr_t)q % 16 == 0 &&
                     (a.ld_x * esz) % 16 == 0 && (a.K * esz) % 16 == 0;
+  if constexpr (SILU && XT == Q8_BF16) if (wave && a.M * a.K >= kSiluTableMinElems) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidDevice;
+    const int64_t need = (total + kSiluThreads - 1) / kSiluThreads;
+    const dim3 grid((unsigned)(need < 2 * cus ? need : 2 * cus)), tblk(kSiluThreads);
+    switch (g / 16) {
+#define Q8_SILU_TABLE_CASE(T)                                                                   \
+  case T:                                                                                       \
+    hipLaunchKernelGGL((quant_silu_bf16_table<FP8, UE, T>), grid, tblk, 0, st, a.x, a.M, a.K,   \
+                       a.ld_x, q, a.s, a.masked_m, max_m, a.eps, a.qmin, a.qmax);               \
+    break;
+      Q8_SILU_TABLE_CASE(1) Q8_SILU_TABLE_CASE(2) Q8_SILU_TABLE_CASE(4) Q8_SILU_TABLE_CASE(8)
+      Q8_SILU_TABLE_CASE(16) Q8_SILU_TABLE_CASE(32)
+#undef Q8_SILU_TABLE_CASE
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if (wave) {
     const dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
     switch (g / 16) {

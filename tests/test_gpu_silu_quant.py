@@ -75,6 +75,46 @@ def test_every_bf16_gate_exactly(up):
     assert np.array_equal(qg, qo)
 
 
+@pytest.mark.parametrize("up", ["one", "random"])
+def test_every_bf16_gate_table_path(up):
+    """The bf16 path of large inputs reads h(g) = g / (1 + exp(-g)) from a
+    table (and closed forms outside it). Groups of 16 equal elements with
+    clipping range [-1, 1] make every stored scale |y| exactly; every finite
+    bf16 gate appears in its own group, the sweep repeated four times to
+    reach the table path's size (2^22 elements)."""
+    K = 1024
+    gates = _all_finite_bf16(65536).float().numpy()
+    gx = np.repeat(gates, 16).reshape(-1, K)                  # 1024 rows
+    if up == "one":
+        ux = np.ones_like(gx)
+    else:
+        r = np.clip(synth.activations(65536, 1, "bf16", sigma=0.5, seed=22).float().numpy()[:, 0],
+                    -1.0, 1.0)
+        ux = np.repeat(r, 16).reshape(-1, K)
+    x = torch.from_numpy(np.concatenate([gx, ux], axis=1)).to(torch.bfloat16).repeat(4, 1)
+    assert x.shape[0] * K == 1 << 22
+    qg, sg = _run(x.to(DEV), K, 16, qmin=-1.0, qmax=1.0, fill=False)
+    qo, so, _ = _oracle(x, 16, qmin=-1.0, qmax=1.0)
+    bad = sg.view(np.uint32) != so.view(np.uint32)
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{int(bad.sum())} scales differ; first group {tuple(i)}: "
+                             f"gpu={sg[tuple(i)]!r} oracle={so[tuple(i)]!r}")
+    assert np.array_equal(qg, qo)
+
+
+def test_masked_rows_table_path():
+    """Masked layout large enough for the table path (8 x 1024 rows of 2 x 512)."""
+    E, max_m, K, g = 8, 1024, 512, 128
+    mm = np.array([0, 1024, 7, 513, 1, 1000, 64, 300], dtype=np.int32)
+    x = synth.activations(E * max_m, 2 * K, "bf16", seed=17).reshape(E, max_m, -1)
+    qg, sg = _run(x.to(DEV), K, g, masked_m=torch.from_numpy(mm).to(DEV))
+    qo, so, valid = _oracle(x, g, masked_m=mm, max_m=max_m)
+    qg, sg = qg.reshape(E * max_m, K), sg.reshape(E * max_m, -1)
+    assert np.array_equal(qg[valid], qo[valid]) and np.array_equal(sg[valid], so[valid])
+    assert np.all(qg[~valid].view(np.uint8) == 0x5A) and np.all(sg[~valid] == -7.0)
+
+
 @pytest.mark.parametrize("xdt", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("g,ue,int8", [(128, False, False), (32, True, False), (16, False, False),
                                        (512, False, False), (128, False, True), (96, False, False),
