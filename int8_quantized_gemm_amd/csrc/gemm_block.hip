@@ -127,14 +127,28 @@ __device__ __forceinline__ void store4(const TileParams& p, int64_t row, int64_t
   }
 }
 
-// BM x BN output tile per workgroup of WM x WN waves; each wave owns a
-// (BM/WM) x (BN/WN) sub-tile made of 16 x 16 MFMA blocks. MFMA operand 0 is
-// the weight fragment and operand 1 the activation fragment, so a lane's
-// four accumulators are four consecutive output columns of one row: one
-// activation-scale value per row block, and 8-byte output stores.
+// Shared memory of one workgroup: two stages of A rows, W rows and
+// activation scales. Two stages in separate arrays: the compiler can then
+// tell that the LDS reads of one stage never alias the in-flight
+// global->LDS loads of the other and does not wait for those loads before
+// computing.
+struct TileSmem {
+  uint8_t* a0; uint8_t* a1; uint8_t* b0; uint8_t* b1; float* s0; float* s1;
+};
+
+// BM x BN output tile [m_lo, m_hi) x [n0, n0 + BN) (of expert e) computed by
+// one workgroup of WM x WN waves; each wave owns a (BM/WM) x (BN/WN) sub-tile
+// made of 16 x 16 MFMA blocks. MFMA operand 0 is the weight fragment and
+// operand 1 the activation fragment, so a lane's four accumulators are four
+// consecutive output columns of one row: one activation-scale value per row
+// block, and 8-byte output stores.
 // WSU: every 16-column block of a wave lies in the same weight-scale block.
+// sm holds stages of at least BM (A) and BN (W) rows; the activation-scale
+// stages, [KSUB][WM][FM/4][16][4], let a lane read its FM row-block scales as
+// FM/4 16-byte vectors, consecutive lanes 16 bytes apart (conflict free).
 template <int BM, int BN, int WM, int WN, int KS, bool GROUPED, bool WSU>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
+__device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int64_t m_hi, int64_t n0,
+                                          int e, const TileSmem& sm) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
@@ -145,19 +159,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
   constexpr int S_PER = (S_SLOTS + NW - 1) / NW;
   static_assert(TM % 16 == 0 && TN % 16 == 0 && FM % 4 == 0, "wave tile");
   static_assert(BM % 8 == 0 && BN % 8 == 0 && (BM * KSUB) % 64 == 0, "tile");
-
-  // Two stages in separate arrays: the compiler can then tell that the LDS
-  // reads of one stage never alias the in-flight global->LDS loads of the
-  // other and does not wait for those loads before computing.
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * 128];
-  // activation scales of a stage, [KSUB][WM][FM/4][16][4]: a lane reads its FM
-  // row-block scales as FM/4 16-byte vectors, consecutive lanes 16 bytes apart
-  // (conflict free)
-  __shared__ __attribute__((aligned(16))) float sS0[KSUB * BM];
-  __shared__ __attribute__((aligned(16))) float sS1[KSUB * BM];
+  uint8_t* const sA0 = sm.a0;
+  uint8_t* const sA1 = sm.a1;
+  uint8_t* const sB0 = sm.b0;
+  uint8_t* const sB1 = sm.b1;
+  float* const sS0 = sm.s0;
+  float* const sS1 = sm.s1;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -165,65 +172,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
   const int g = lane >> 4, r16 = lane & 15;
   const int64_t N = p.N, K = p.K;
   const int KB = p.KB;
-
-  // ---- which tile
-  int64_t m_lo, m_hi, n0;
-  int e = 0;
-  if constexpr (GROUPED) {
-    // (expert, m tile, n tile) of this workgroup from the experts' row
-    // offsets, 64 experts at a time across the lanes of every wave (a serial
-    // walk over the experts would cost one dependent load per expert): a
-    // reduction gives the number of tiles, an inclusive scan and a ballot
-    // find the expert whose tiles contain this one. The host keeps the tile
-    // count below 2^31.
-    auto tiles_of = [&](int x) -> int {
-      if (x >= p.E) return 0;
-      return ((p.offsets[x + 1] - p.offsets[x] + BM - 1) / BM) * (int)p.tiles_n;
-    };
-    int total = 0;
-    for (int c = 0; c < p.E; c += 64) {
-      int t = tiles_of(c + lane);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, 64);
-      total += t;
-    }
-    total = __builtin_amdgcn_readfirstlane(total);
-    if ((int)blockIdx.x >= total) return;
-    int L = (int)xcd_remap(blockIdx.x, total);
-    int base = 0, mt = 1;
-    for (int c = 0; c < p.E; c += 64) {
-      const int t = tiles_of(c + lane);
-      int incl = t;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
-      }
-      const int chunk = __shfl(incl, 63, 64);
-      if (L < base + chunk) {
-        const int le = __builtin_ctzll(__ballot(base + incl > L));
-        e = c + le;
-        L -= base + __shfl(incl - t, le, 64);
-        mt = __shfl(t, le, 64) / (int)p.tiles_n;
-        break;
-      }
-      base += chunk;
-    }
-    e = __builtin_amdgcn_readfirstlane(e);
-    L = __builtin_amdgcn_readfirstlane(L);
-    mt = __builtin_amdgcn_readfirstlane(mt);
-    const int64_t tn = L / mt, tm = L - tn * mt;
-    m_lo = p.offsets[e] + tm * BM;
-    m_hi = m_lo + BM < p.offsets[e + 1] ? m_lo + BM : p.offsets[e + 1];
-    n0 = tn * BN;
-  } else {
-    const int64_t t = xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n);
-    int64_t tm, tn;
-    grouped_order(t, p.tiles_m, p.tiles_n, 8, tm, tn);
-    m_lo = tm * BM;
-    m_hi = m_lo + BM < p.M ? m_lo + BM : p.M;
-    n0 = tn * BN;
-  }
   const uint8_t* Wb = p.W + (GROUPED ? (int64_t)e * N * K : 0);
   const float* Wsb = p.Ws + (GROUPED ? (int64_t)e * p.nbw * KB : 0);
 
@@ -440,6 +388,81 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
       store4(p, drow, n, acc[i][j], bf16, vec);
     }
   }
+}
+
+#define Q8_TILE_SMEM(BM, BN, KSUB)                                        \
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0_[(BM) * 128];     \
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1_[(BM) * 128];     \
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0_[(BN) * 128];     \
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1_[(BN) * 128];     \
+  __shared__ __attribute__((aligned(16))) float sS0_[(KSUB) * (BM)];      \
+  __shared__ __attribute__((aligned(16))) float sS1_[(KSUB) * (BM)];      \
+  const TileSmem sm{sA0_, sA1_, sB0_, sB1_, sS0_, sS1_}
+
+// One tile shape over the whole output (dense), or over the experts' row
+// ranges (GROUPED).
+template <int BM, int BN, int WM, int WN, int KS, bool GROUPED, bool WSU>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
+  Q8_TILE_SMEM(BM, BN, 128 / KS);
+  const int lane = threadIdx.x & 63;
+  int64_t m_lo, m_hi, n0;
+  int e = 0;
+  if constexpr (GROUPED) {
+    // (expert, m tile, n tile) of this workgroup from the experts' row
+    // offsets, 64 experts at a time across the lanes of every wave (a serial
+    // walk over the experts would cost one dependent load per expert): a
+    // reduction gives the number of tiles, an inclusive scan and a ballot
+    // find the expert whose tiles contain this one. The host keeps the tile
+    // count below 2^31.
+    auto tiles_of = [&](int x) -> int {
+      if (x >= p.E) return 0;
+      return ((p.offsets[x + 1] - p.offsets[x] + BM - 1) / BM) * (int)p.tiles_n;
+    };
+    int total = 0;
+    for (int c = 0; c < p.E; c += 64) {
+      int t = tiles_of(c + lane);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, 64);
+      total += t;
+    }
+    total = __builtin_amdgcn_readfirstlane(total);
+    if ((int)blockIdx.x >= total) return;
+    int L = (int)xcd_remap(blockIdx.x, total);
+    int base = 0, mt = 1;
+    for (int c = 0; c < p.E; c += 64) {
+      const int t = tiles_of(c + lane);
+      int incl = t;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      const int chunk = __shfl(incl, 63, 64);
+      if (L < base + chunk) {
+        const int le = __builtin_ctzll(__ballot(base + incl > L));
+        e = c + le;
+        L -= base + __shfl(incl - t, le, 64);
+        mt = __shfl(t, le, 64) / (int)p.tiles_n;
+        break;
+      }
+      base += chunk;
+    }
+    e = __builtin_amdgcn_readfirstlane(e);
+    L = __builtin_amdgcn_readfirstlane(L);
+    mt = __builtin_amdgcn_readfirstlane(mt);
+    const int64_t tn = L / mt, tm = L - tn * mt;
+    m_lo = p.offsets[e] + tm * BM;
+    m_hi = m_lo + BM < p.offsets[e + 1] ? m_lo + BM : p.offsets[e + 1];
+    n0 = tn * BN;
+  } else {
+    const int64_t t = xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n);
+    int64_t tm, tn;
+    grouped_order(t, p.tiles_m, p.tiles_n, 8, tm, tn);
+    m_lo = tm * BM;
+    m_hi = m_lo + BM < p.M ? m_lo + BM : p.M;
+    n0 = tn * BN;
+  }
+  tile_body<BM, BN, WM, WN, KS, GROUPED, WSU>(p, m_lo, m_hi, n0, e, sm);
 }
 
 // ------------------------------------------------------------------------------
