@@ -509,7 +509,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-rows", type=int, default=4096, help="prefill rows for the oracle baseline")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run prefill GEMM launches and a 256 MiB device copy (for HBM counters)")

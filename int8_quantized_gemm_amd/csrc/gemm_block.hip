@@ -686,6 +686,30 @@ __global__ __launch_bounds__(NW * 64) void gemm_stream(TileParams p) {
 // ------------------------------------------------------------------------------
 // Streaming (decode) kernel with shared activations: M <= 16, K a multiple of 1024
 // ------------------------------------------------------------------------------
+// Fragment layout of gemm_stream_sa: lane group g holds bytes [16g, 16g+16)
+// (first half) and [64+16g, 64+16g+16) (second half) of each 128-byte chunk,
+// so each load instruction reads a contiguous 64-byte half of sixteen weight
+// rows (measured: M = 16 10.9 -> 10.5 us against 32-byte lane pieces).
+__device__ __forceinline__ i32x8 gload_halves(const uint8_t* p) {
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 64);
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// The part of such a fragment that belongs to 32-wide K block s of the chunk:
+// the half s>>1 of the lane groups with g>>1 == s&1; everything else zeroed.
+__device__ __forceinline__ i32x8 block32_part(const i32x8& f, int s, int g) {
+  const bool mine = (g >> 1) == (s & 1);
+  const bool hi = (s >> 1) != 0;
+  i32x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = (mine && !hi) ? f[i] : 0;
+    r[4 + i] = (mine && hi) ? f[4 + i] : 0;
+  }
+  return r;
+}
+
 // Every workgroup needs all M activation rows and their scales. Read from L2
 // by every wave, those few lines are requested by thousands of waves at once
 // and serialise on their L2 channels; here one linear pass per workgroup
@@ -736,13 +760,13 @@ void gemm_stream_sa(TileParams p) {
   const float wsl = wsp[kb_l];
   asm volatile("" ::: "memory");
   const int64_t nrow = n0 + r16 < N ? n0 + r16 : N - 1;
-  const uint8_t* wp = p.W + nrow * K + 32 * g;
+  const uint8_t* wp = p.W + nrow * K + 16 * g;
   i32x8 wf[R];
 #pragma unroll
   for (int u = 0; u < R; ++u) {
     // unconditional (clamped) loads: exactly 2R of them follow the copies
     const int c = c_b + u < NC - 1 ? c_b + u : NC - 1;
-    wf[u] = gload32(wp + (int64_t)c * 128);
+    wf[u] = gload_halves(wp + (int64_t)c * 128);
   }
   // the copies were issued before the 2R weight loads, and loads complete in
   // order: at most 2R outstanding means this wave's copies have landed. The
@@ -752,16 +776,15 @@ void gemm_stream_sa(TileParams p) {
   asm volatile("" ::: "memory");
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  const i32x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
   const int arow = r16 < M ? r16 : (int)M - 1;  // rows past M repeat the last (never stored)
-  const uint8_t* al = sA + arow * a_pitch + 32 * g;
+  const uint8_t* al = sA + arow * a_pitch + 16 * g;
   const float* sl = reinterpret_cast<const float*>(sS) + arow * KB;
 #pragma unroll
   for (int u = 0; u < R; ++u) {
     const int c = c_b + u;
     if (c >= c_e) break;
     const i32x4 lo = *reinterpret_cast<const i32x4*>(al + c * 128);
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(al + c * 128 + 16);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(al + c * 128 + 64);
     const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     f32x4 sa;
     if constexpr (KSUB == 4) sa = *reinterpret_cast<const f32x4*>(sl + c * 4);
@@ -769,7 +792,7 @@ void gemm_stream_sa(TileParams p) {
 #pragma unroll
     for (int s = 0; s < KSUB; ++s) {
       const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsl), u * KSUB + s));
-      const i32x8 a = (KS == 128 || g == s) ? af : zero8;
+      const i32x8 a = KS == 128 ? af : block32_part(af, s, g);
       const f32x4 pr = mfma_fp8_k128(wf[u], a);
       acc = fma4s(pr, sa[s] * ws, acc);
     }
