@@ -25,6 +25,8 @@
 //             slot, so a lane's four outputs share one activation row and
 //             one scale product), and the waves' float32 partials are summed
 //             in a fixed order through LDS (deterministic).
+#include <type_traits>
+
 #include "q8_internal.h"
 #include "tile_common.h"
 
@@ -359,14 +361,104 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
     compute(la, lb, ls, wcur);
   };
   const int KT = (int)(K / 128);
-  load_ws(0);
-  issue(0, sA0, sB0, sS0);
-  for (int kt = 0; kt < KT; ++kt) {
+  if (KS == 128 && WSU && !GROUPED && KB <= 64) {
+    // 128-wide K blocks: the last row block of each slab is computed after
+    // the slab barrier, behind the LDS reads of the next slab's weight
+    // fragments and first activation fragment (issued right after the
+    // barrier into a second set of registers), so those reads are in flight
+    // while the matrix cores work instead of before the first MFMA of the
+    // slab. MFMA results are folded into the accumulators two MFMAs after
+    // issue through a ring of three, which frees the registers for the second
+    // fragment set. Slabs alternate between stage 0 and stage 1 with the loop
+    // unrolled by two, so every LDS address names its stage array and the
+    // compiler sees that the refill of one stage never aliases reads of the
+    // other.
+    constexpr int NT = FM * FN;  // MFMAs per slab and wave
+    struct SlabRegs {
+      i32x8 bw[FN];
+      float sa[FM];
+      float ws[1];
+    };
+    SlabRegs R0, R1;
+    i32x8 av[2];
+    f32x4 pr[3];
+    // the wave's weight scales of all K blocks, one per lane (KB <= 64),
+    // loaded once: slab kt takes lane kt's with a readlane, so no load of a
+    // scale (and no wait for one) sits in the slab loop
+    const float wsl = Wsb[ws_idx[0] + (lane < KB ? lane : KB - 1)];
+    auto slab_start = [&](SlabRegs& r, int kt, const uint8_t* __restrict__ lb,
+                          const float* __restrict__ ls) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) r.bw[j] = lds_frag32(lb, wn * TN + j * 16 + r16, g);
+#pragma unroll
+      for (int i4 = 0; i4 < FM / 4; ++i4) {
+        const f32x4 q = *reinterpret_cast<const f32x4*>(ls + wm * TM + (i4 * 16 + r16) * 4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r.sa[4 * i4 + c] = q[c];
+      }
+      r.ws[0] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsl), kt));
+    };
+    auto fold = [&](const SlabRegs& r, int n) {
+      const int i = n / FN, j = n % FN;
+      acc[i][j] = fma4s(pr[n % 3], r.sa[i] * r.ws[0], acc[i][j]);
+      // pins the fold here: otherwise it is sunk past the slab barrier, to its
+      // next use, and every MFMA result of the slab stays live until then
+      asm volatile("" : "+v"(acc[i][j]));
+    };
+    // B0, E0: std::integral_constant bounds, so the loop is unrolled with
+    // every register index a constant
+    auto rows = [&](const SlabRegs& r, const uint8_t* __restrict__ la, auto B0, auto E0) {
+      constexpr int n0_ = decltype(B0)::value, n1_ = decltype(E0)::value;
+#pragma unroll
+      for (int n = n0_; n < n1_; ++n) {
+        const int i = n / FN, j = n % FN;
+        if (j == 0 && i + 1 < FM) av[(i + 1) & 1] = lds_frag32(la, wm * TM + (i + 1) * 16 + r16, g);
+        pr[n % 3] = mfma_fp8_k128(r.bw[j], av[i & 1]);
+        if (n >= 2) fold(r, n - 2);
+        // keep this order: hoisting the MFMAs ahead of the folds would keep
+        // every result live at once
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // one slab: rows 0 .. FM-2, the barrier and the next slab's first reads
+    // (plus the refill of this slab's stage with slab kt + 2), then row FM-1
+    auto slab = [&](int kt, SlabRegs& cur, SlabRegs& nxt, uint8_t* __restrict__ la,
+                    uint8_t* __restrict__ lb, float* __restrict__ ls, const uint8_t* __restrict__ na,
+                    const uint8_t* __restrict__ nb, const float* __restrict__ ns) {
+      rows(cur, la, std::integral_constant<int, 0>{}, std::integral_constant<int, NT - FN>{});
+      if (kt + 1 < KT) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmem();
+        __syncthreads();
+        slab_start(nxt, kt + 1, nb, ns);
+        av[0] = lds_frag32(na, wm * TM + r16, g);
+        if (kt + 2 < KT) issue(kt + 2, la, lb, ls);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      rows(cur, la, std::integral_constant<int, NT - FN>{}, std::integral_constant<int, NT>{});
+      fold(cur, NT - 2);
+      fold(cur, NT - 1);
+    };
+    issue(0, sA0, sB0, sS0);
     wait_vmem();
     __syncthreads();
-    const bool odd = kt & 1;
-    step(kt, kt + 1 < KT, odd ? sA0 : sA1, odd ? sB0 : sB1, odd ? sS0 : sS1,
-         odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sS1 : sS0);
+    slab_start(R0, 0, sB0, sS0);
+    av[0] = lds_frag32(sA0, wm * TM + r16, g);
+    if (KT > 1) issue(1, sA1, sB1, sS1);
+    for (int kt = 0; kt < KT; kt += 2) {
+      slab(kt, R0, R1, sA0, sB0, sS0, sA1, sB1, sS1);
+      if (kt + 1 < KT) slab(kt + 1, R1, R0, sA1, sB1, sS1, sA0, sB0, sS0);
+    }
+  } else {
+    load_ws(0);
+    issue(0, sA0, sB0, sS0);
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_vmem();
+      __syncthreads();
+      const bool odd = kt & 1;
+      step(kt, kt + 1 < KT, odd ? sA0 : sA1, odd ? sB0 : sB1, odd ? sS0 : sS1,
+           odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sS1 : sS0);
+    }
   }
 
   // ---- epilogue: lane holds D[row, n .. n+3], row = block row r16
