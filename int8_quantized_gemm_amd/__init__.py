@@ -112,16 +112,19 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else t.data_ptr()
 
 
-def _dev(*ts) -> torch.device:
-    dev = None
+def _dev(*ts) -> int:
+    """Index of the one GPU every given tensor lives on (integer indices: the
+    launch path runs once per kernel, and torch.device objects cost time)."""
+    dev = -1
     for t in ts:
         if t is None:
             continue
-        if not t.is_cuda:
+        d = t.get_device()
+        if d < 0:
             raise ValueError("every tensor must be on the GPU")
-        if dev is None:
-            dev = t.device
-        elif t.device != dev:
+        if dev < 0:
+            dev = d
+        elif d != dev:
             raise ValueError("tensors on different devices")
     return dev
 
@@ -132,11 +135,27 @@ def _contig(*ts) -> None:
             raise ValueError("tensor must be contiguous")
 
 
-def _stream(dev) -> int:
-    return torch.cuda.current_stream(dev).cuda_stream
+def _stream(dev: int) -> int:
+    """Raw handle of torch's current stream on device ``dev`` (no Stream object)."""
+    return torch._C._cuda_getCurrentRawStream(dev)
 
 
 _ws_cache: dict = {}
+
+
+_ws_sizes: dict = {}
+
+
+def _ws_size(fn, *args) -> int:
+    """A workspace-size query of the library, memoised per shape (each query is
+    a ctypes call, which costs about a microsecond on the launch path)."""
+    key = (fn.__name__, args)
+    n = _ws_sizes.get(key)
+    if n is None:
+        n = fn(*args)
+        if len(_ws_sizes) < 4096:
+            _ws_sizes[key] = n
+    return n
 
 
 def _workspace(dev, nbytes: int):
@@ -191,7 +210,7 @@ def quant_8bit(input: torch.Tensor, output_q: torch.Tensor, output_s: torch.Tens
         raise ValueError("fuse_silu_and_mul needs an even input width")
     if tuple(output_q.shape) != (M, K):
         raise ValueError("output_q must be [M, K] (K = half the input width when fused)")
-    ws, wsb = _workspace(dev, _quant_ws(M, K, mode))
+    ws, wsb = _workspace(dev, _ws_size(_quant_ws, M, K, mode))
     _check(_quant(_ptr(input), _dt(input.dtype), M, K, input.stride(0) if M > 1 else Kin,
                   _ptr(output_q), _dt(output_q.dtype), _ptr(output_s), group_size, mode, eps,
                   fp8_min, fp8_max, int(scale_ue8m0), int(fuse_silu_and_mul), _ptr(masked_m),
@@ -214,7 +233,7 @@ def blockwise_scaled_mm(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torc
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=dev)
     _contig(out)
-    ws, wsb = _workspace(dev, _bmm_ws(M, N, K, bn, bk))
+    ws, wsb = _workspace(dev, _ws_size(_bmm_ws, M, N, K, bn, bk))
     _check(_bmm(_ptr(mat_a), _ptr(scales_a), _ptr(mat_b), _ptr(scales_b), _ptr(bias), _ptr(out),
                 _dt(out.dtype), M, N, K, bn, bk, ws, wsb, _stream(dev)))
     return out
