@@ -95,6 +95,15 @@ def test_tile_shapes_ragged(M, N, K, bk):
     run_case(M, N, K, bk, bk, ue=(bk == 32), bias=True, seed=M + N)
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 256, 128), (130, 512, 8192), (130, 300, 8320), (257, 520, 640)])
+def test_tile_k_extent(M, N, K):
+    """K extents of the 128-wide-block tile kernel's slab loops: a single slab
+    (K = 128), the most K blocks whose weight scales one lane register holds
+    (K = 8192, 64 blocks), one more (K = 8320, the other loop), and an odd
+    slab count (K = 640)."""
+    run_case(M, N, K, 128, 128, bias=True, seed=K)
+
+
 @pytest.mark.parametrize("bn", [48, 64, 256])
 def test_weight_block_rows_differ_from_bk(bn):
     run_case(200, 600, 512, bn, 128, seed=3)
