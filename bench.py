@@ -481,10 +481,11 @@ class _Null:
 
 
 def traffic_probe(torch, q8, synth) -> int:
-    """Kernels for the HBM byte counters: three prefill GEMM launches (inputs
-    written fresh each time so they are not resident in the Infinity Cache)
-    and three plain 256 MiB device-to-device copies of known size (the scale
-    for FETCH_SIZE / WRITE_SIZE)."""
+    """Kernels for the HBM byte counters: three prefill GEMM launches and three
+    decode GEMM launches at M=1 and at M=16 (a 256 MiB fill before each, so the
+    operands are not resident in the Infinity Cache), and three plain 256 MiB
+    device-to-device copies of known size (the scale for FETCH_SIZE /
+    WRITE_SIZE)."""
     M, N, K, blk = 4096, 7168, 7168, 128
     dev = "cuda:0"
     x = synth.activations(M, K, "bf16", seed=0).to(dev)
@@ -500,10 +501,25 @@ def traffic_probe(torch, q8, synth) -> int:
         q8.quant_8bit(x, aq, As, blk, EPS, -448.0, 448.0, False)
         big.fill_(1)  # evict: 256 MiB written between launches
         q8.blockwise_scaled_mm(aq, Wq, As, Ws, torch.bfloat16, block=(blk, blk), out=D)
+    # decode block32 GEMMs (N=4096, K=7168): M=1 (weight-streaming kernel) and
+    # M=16 (the kernel that stages the activations in LDS)
+    Nd, db = 4096, 32
+    Wd, Wsd = synth.fp8_block_weights(Nd, K, db, db, seed=0)
+    Wd, Wsd = Wd.to(dev), Wsd.to(dev)
+    for Md in (1, 16):
+        xd = synth.activations(Md, K, "bf16", outlier_frac=0.01, seed=0).to(dev)
+        aqd = torch.empty((Md, K), dtype=torch.float8_e4m3fn, device=dev)
+        Asd = torch.empty((Md, K // db), dtype=torch.float32, device=dev)
+        Dd = torch.empty((Md, Nd), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            q8.quant_8bit(xd, aqd, Asd, db, EPS, -448.0, 448.0, True)
+            big.fill_(1)
+            q8.blockwise_scaled_mm(aqd, Wd, Asd, Wsd, torch.bfloat16, block=(db, db), out=Dd)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    log("traffic probe done: 3 GEMM launches, 3 copies of 268435456 bytes")
+    log("traffic probe done: 3 prefill GEMM launches, 3 decode GEMM launches each at M=1 and M=16, "
+        "3 copies of 268435456 bytes")
     return 0
 
 
