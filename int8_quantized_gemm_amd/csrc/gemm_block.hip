@@ -361,7 +361,24 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
     compute(la, lb, ls, wcur);
   };
   const int KT = (int)(K / 128);
-  if (KS == 128 && WSU && !GROUPED && KB <= 64) {
+  // the loop used for K blocks of 128, one weight-scale block per wave, dense
+  // tiles and up to 64 K blocks; every other case takes the general loop below
+  auto general_loop = [&]() {
+    load_ws(0);
+    issue(0, sA0, sB0, sS0);
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_vmem();
+      __syncthreads();
+      const bool odd = kt & 1;
+      step(kt, kt + 1 < KT, odd ? sA0 : sA1, odd ? sB0 : sB1, odd ? sS0 : sS1,
+           odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sS1 : sS0);
+    }
+  };
+  if constexpr (!(KS == 128 && WSU && !GROUPED)) {
+    general_loop();
+  } else if (KB > 64) {
+    general_loop();
+  } else {
     // 128-wide K blocks: the last row block of each slab is computed after
     // the slab barrier, behind the LDS reads of the next slab's weight
     // fragments and first activation fragment (issued right after the
@@ -448,16 +465,6 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
     for (int kt = 0; kt < KT; kt += 2) {
       slab(kt, R0, R1, sA0, sB0, sS0, sA1, sB1, sS1);
       if (kt + 1 < KT) slab(kt + 1, R1, R0, sA1, sB1, sS1, sA0, sB0, sS0);
-    }
-  } else {
-    load_ws(0);
-    issue(0, sA0, sB0, sS0);
-    for (int kt = 0; kt < KT; ++kt) {
-      wait_vmem();
-      __syncthreads();
-      const bool odd = kt & 1;
-      step(kt, kt + 1 < KT, odd ? sA0 : sA1, odd ? sB0 : sB1, odd ? sS0 : sS1,
-           odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sS1 : sS0);
     }
   }
 
