@@ -205,7 +205,12 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
     for (int r = tid; r < BM; r += NW * 64) sAoff[r] = (uint32_t)(a_row(m_lo + r) * K);
     __syncthreads();
   }
-  const uint32_t chunk_off = lane_off - (uint32_t)((lane >> 3) * K);
+  // the lane's chunk within its row (grouped loads add the row from the table)
+  auto chunk_off = [&]() -> uint32_t {
+    uint32_t c = (uint32_t)(((lane & 7) ^ ((4 * (w & 1) + (lane >> 4)) & 7)) << 4);
+    if constexpr (GROUPED) asm volatile("" : "+v"(c));  // recomputed per use, not held live
+    return c;
+  };
   uint32_t s_off[S_PER];
   // scale loads: waves past the last slot repeat an earlier slot (same bytes
   // to the same place), so every wave issues the same instruction stream
@@ -225,12 +230,16 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
   const uint32_t a_base = GROUPED ? 0u : (uint32_t)(m_lo * K);
   const uint32_t b_base = (uint32_t)(n0 * K);
   auto issue = [&](int kt, uint8_t* __restrict__ la, uint8_t* __restrict__ lb, float* __restrict__ ls) {
+    // grouped: one table index per lane, recomputed here; the loads below
+    // add constant offsets to it (entry 8q + l/8 for q = w + c*NW)
+    uint32_t tix = (uint32_t)(8 * w + (lane >> 3));
+    if constexpr (GROUPED) asm volatile("" : "+v"(tix));
 #pragma unroll
     for (int c = 0; c < A_PER; ++c) {
       const int q = w + c * NW;
       if (A_SLOTS % NW == 0 || q < A_SLOTS) {
         if constexpr (GROUPED)
-          b2l16(rA, sAoff[8 * q + (lane >> 3)] + chunk_off, kt * 128, la + q * 1024);
+          b2l16(rA, sAoff[tix + 8 * NW * c] + chunk_off(), kt * 128, la + q * 1024);
         else
           b2l16(rA, lane_off, a_base + (uint32_t)(8 * q) * (uint32_t)K + kt * 128, la + q * 1024);
       }
@@ -239,7 +248,8 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
     for (int c = 0; c < B_PER; ++c) {
       const int q = w + c * NW;
       if (B_SLOTS % NW == 0 || q < B_SLOTS)
-        b2l16(rB, lane_off, b_base + (uint32_t)(8 * q) * (uint32_t)K + kt * 128, lb + q * 1024);
+        b2l16(rB, GROUPED ? (uint32_t)((lane >> 3) * K) + chunk_off() : lane_off,
+              b_base + (uint32_t)(8 * q) * (uint32_t)K + kt * 128, lb + q * 1024);
     }
 #pragma unroll
     for (int c = 0; c < S_PER; ++c) b2l4(rS, s_off[c], kt * KSUB * 4, ls + ((w + c * NW) % S_SLOTS) * 64);
@@ -361,8 +371,8 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
     compute(la, lb, ls, wcur);
   };
   const int KT = (int)(K / 128);
-  // the loop used for K blocks of 128, one weight-scale block per wave, dense
-  // tiles and up to 64 K blocks; every other case takes the general loop below
+  // the loop used for K blocks of 128, one weight-scale block per wave and up
+  // to 64 K blocks; every other case takes the general loop below
   auto general_loop = [&]() {
     load_ws(0);
     issue(0, sA0, sB0, sS0);
@@ -374,7 +384,7 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
            odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sS1 : sS0);
     }
   };
-  if constexpr (!(KS == 128 && WSU && !GROUPED)) {
+  if constexpr (!(KS == 128 && WSU)) {
     general_loop();
   } else if (KB > 64) {
     general_loop();
@@ -447,9 +457,16 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
         __builtin_amdgcn_sched_barrier(0);
         wait_vmem();
         __syncthreads();
+        // grouped tiles: the refill first (its row-table lookups then retire
+        // before the fragment registers fill up)
+        if constexpr (GROUPED) {
+          if (kt + 2 < KT) issue(kt + 2, la, lb, ls);
+        }
         slab_start(nxt, kt + 1, nb, ns);
         av[0] = lds_frag32(na, wm * TM + r16, g);
-        if (kt + 2 < KT) issue(kt + 2, la, lb, ls);
+        if constexpr (!GROUPED) {
+          if (kt + 2 < KT) issue(kt + 2, la, lb, ls);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       rows(cur, la, std::integral_constant<int, NT - FN>{}, std::integral_constant<int, NT>{});
