@@ -229,9 +229,10 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(p.As, p.as_bytes);
   const uint32_t a_base = GROUPED ? 0u : (uint32_t)(m_lo * K);
   const uint32_t b_base = (uint32_t)(n0 * K);
-  auto issue = [&](int kt, uint8_t* __restrict__ la, uint8_t* __restrict__ lb, float* __restrict__ ls) {
-    // grouped: one table index per lane, recomputed here; the loads below
-    // add constant offsets to it (entry 8q + l/8 for q = w + c*NW)
+  // one slab's global->LDS copies, by operand: A rows, W rows, activation
+  // scales. Grouped: one table index per lane, recomputed per call; the loads
+  // add constant offsets to it (entry 8q + l/8 for q = w + c*NW)
+  auto issue_a = [&](int kt, uint8_t* __restrict__ la) {
     uint32_t tix = (uint32_t)(8 * w + (lane >> 3));
     if constexpr (GROUPED) asm volatile("" : "+v"(tix));
 #pragma unroll
@@ -244,6 +245,8 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
           b2l16(rA, lane_off, a_base + (uint32_t)(8 * q) * (uint32_t)K + kt * 128, la + q * 1024);
       }
     }
+  };
+  auto issue_w = [&](int kt, uint8_t* __restrict__ lb) {
 #pragma unroll
     for (int c = 0; c < B_PER; ++c) {
       const int q = w + c * NW;
@@ -251,8 +254,15 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
         b2l16(rB, GROUPED ? (uint32_t)((lane >> 3) * K) + chunk_off() : lane_off,
               b_base + (uint32_t)(8 * q) * (uint32_t)K + kt * 128, lb + q * 1024);
     }
+  };
+  auto issue_s = [&](int kt, float* __restrict__ ls) {
 #pragma unroll
     for (int c = 0; c < S_PER; ++c) b2l4(rS, s_off[c], kt * KSUB * 4, ls + ((w + c * NW) % S_SLOTS) * 64);
+  };
+  auto issue = [&](int kt, uint8_t* __restrict__ la, uint8_t* __restrict__ lb, float* __restrict__ ls) {
+    issue_a(kt, la);
+    issue_w(kt, lb);
+    issue_s(kt, ls);
   };
 
   // weight-scale rows of this wave's 16-column blocks (clamped for ragged N);
@@ -433,12 +443,17 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
       asm volatile("" : "+v"(acc[i][j]));
     };
     // B0, E0: std::integral_constant bounds, so the loop is unrolled with
-    // every register index a constant
-    auto rows = [&](const SlabRegs& r, const uint8_t* __restrict__ la, auto B0, auto E0) {
+    // every register index a constant; wkt >= 0 issues the W rows of slab
+    // wkt into wdst at step W_STEP (wkt < 0: none)
+    constexpr int W_STEP = 12;
+    static_assert(W_STEP < NT - FN, "the W refill must go out before the slab barrier");
+    auto rows = [&](const SlabRegs& r, const uint8_t* __restrict__ la, auto B0, auto E0, int wkt,
+                    uint8_t* __restrict__ wdst) {
       constexpr int n0_ = decltype(B0)::value, n1_ = decltype(E0)::value;
 #pragma unroll
       for (int n = n0_; n < n1_; ++n) {
         const int i = n / FN, j = n % FN;
+        if (n == W_STEP && wkt >= 0) issue_w(wkt, wdst);
         if (j == 0 && i + 1 < FM) av[(i + 1) & 1] = lds_frag32(la, wm * TM + (i + 1) * 16 + r16, g);
         pr[n % 3] = mfma_fp8_k128(r.bw[j], av[i & 1]);
         if (n >= 2) fold(r, n - 2);
@@ -452,7 +467,10 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
     auto slab = [&](int kt, SlabRegs& cur, SlabRegs& nxt, uint8_t* __restrict__ la,
                     uint8_t* __restrict__ lb, float* __restrict__ ls, const uint8_t* __restrict__ na,
                     const uint8_t* __restrict__ nb, const float* __restrict__ ns) {
-      rows(cur, la, std::integral_constant<int, 0>{}, std::integral_constant<int, NT - FN>{});
+      // dense tiles: the W rows of slab kt + 1 go out mid-slab (its A rows and
+      // scales went out at the last barrier); grouped tiles refill whole slabs
+      rows(cur, la, std::integral_constant<int, 0>{}, std::integral_constant<int, NT - FN>{},
+           !GROUPED && kt >= 1 && kt + 1 < KT ? kt + 1 : -1, const_cast<uint8_t*>(nb));
       if (kt + 1 < KT) {
         __builtin_amdgcn_sched_barrier(0);
         wait_vmem();
@@ -465,11 +483,14 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
         slab_start(nxt, kt + 1, nb, ns);
         av[0] = lds_frag32(na, wm * TM + r16, g);
         if constexpr (!GROUPED) {
-          if (kt + 2 < KT) issue(kt + 2, la, lb, ls);
+          if (kt + 2 < KT) {
+            issue_a(kt + 2, la);
+            issue_s(kt + 2, ls);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      rows(cur, la, std::integral_constant<int, NT - FN>{}, std::integral_constant<int, NT>{});
+      rows(cur, la, std::integral_constant<int, NT - FN>{}, std::integral_constant<int, NT>{}, -1, nullptr);
       fold(cur, NT - 2);
       fold(cur, NT - 1);
     };
