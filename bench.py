@@ -154,6 +154,41 @@ def bench_prefill(torch, q8, synth, steps, warmup):
     }
 
 
+def bench_prefill_variants(torch, q8, synth, pre, reps):
+    """The other two prefill GEMM workloads: the same activation against a
+    [18432, 7168] weight, and the headline shape with a bf16 bias added in the
+    epilogue. GEMM only (the activation is quantized once, beforehand)."""
+    M, _, K, blk = pre["shape"]
+    dev = "cuda:0"
+    aq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+    As = torch.empty((M, K // blk), dtype=torch.float32, device=dev)
+    q8.quant_8bit(pre["x"], aq, As, blk, EPS, -448.0, 448.0, False)
+    out = {}
+    for name, N, with_bias in (("4096x18432x7168", 18432, False), ("4096x7168x7168_bias", 7168, True)):
+        if N == pre["shape"][1]:
+            Wq, Ws = pre["Wq"], pre["Ws"]
+        else:
+            Wq, Ws = synth.fp8_block_weights(N, K, blk, blk, seed=0)
+            Wq, Ws = Wq.to(dev), Ws.to(dev)
+        b = synth.bias(N, seed=0).to(dev) if with_bias else None
+        D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        gt = KernelTimer(torch)
+        for i in range(reps + 5):
+            if i >= 5:
+                with gt:
+                    q8.blockwise_scaled_mm(aq, Wq, As, Ws, torch.bfloat16, bias=b, block=(blk, blk), out=D)
+            else:
+                q8.blockwise_scaled_mm(aq, Wq, As, Ws, torch.bfloat16, bias=b, block=(blk, blk), out=D)
+        torch.cuda.synchronize()
+        g = gt.us()
+        tf = 2.0 * M * N * K / (g["median"] * 1e-6) / 1e12
+        out[name] = {"gemm_us": round(g["median"], 2), "gemm_us_p10": round(g["p10"], 2),
+                     "gemm_us_p90": round(g["p90"], 2), "TFLOP/s": round(tf, 1),
+                     "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+        del D, b
+    return out
+
+
 def batched_us(torch, launch, copies, reps, warmup=3):
     """Per-launch time of ``copies`` back-to-back launches (each on its own
     buffers) between one pair of HIP events on the launch stream, median over
@@ -587,6 +622,8 @@ def main() -> int:
     paths = {"prefill_quant_us": {k: round(v, 2) for k, v in pre["quant_us"].items()}}
     if not args.skip_secondary:
         reps = max(args.steps, 50)
+        paths["prefill_gemm"] = bench_prefill_variants(torch, q8, synth, pre, reps)
+        log(f"prefill variants: {json.dumps(paths['prefill_gemm'])}")
         paths["decode_block32"] = bench_decode(torch, q8, synth, 30)
         log(f"decode: {json.dumps(paths['decode_block32'])}")
         paths["quant_4096x7168"] = bench_quant(torch, q8, synth, 30)

@@ -103,18 +103,13 @@ __device__ __forceinline__ long lds_frag8(const uint8_t* base, int row, int s, i
   return *reinterpret_cast<const long*>(base + swz(row, 2 * s + (g >> 1)) + (g & 1) * 8);
 }
 
-// Store four consecutive outputs D[row, n .. n+3] (+ bias) as 16-bit values.
+// Store four consecutive outputs D[row, n .. n+3] as 16-bit values (any bias
+// already added).
 __device__ __forceinline__ void store4(const TileParams& p, int64_t row, int64_t n, f32x4 v,
                                        bool bf16, bool vec) {
   uint16_t* D = static_cast<uint16_t*>(p.D);
   const int64_t N = p.N;
   if (vec && n + 3 < N) {
-    if (p.bias) {
-      const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.bias) + n);
-      const uint32_t bw[4] = {b.x & 0xFFFFu, b.x >> 16, b.y & 0xFFFFu, b.y >> 16};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] += bf16 ? bf16_bits_to_f32(bw[r]) : f16_bits_to_f32(bw[r]);
-    }
     uint2 o;
     o.x = (uint32_t)to_out_bits(v[0], bf16) | ((uint32_t)to_out_bits(v[1], bf16) << 16);
     o.y = (uint32_t)to_out_bits(v[2], bf16) | ((uint32_t)to_out_bits(v[3], bf16) << 16);
@@ -123,8 +118,7 @@ __device__ __forceinline__ void store4(const TileParams& p, int64_t row, int64_t
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (n + r >= N) break;
-      const float bv = p.bias ? load_out_f32(p.bias, n + r, bf16) : 0.0f;
-      D[row * N + n + r] = to_out_bits(v[r] + bv, bf16);
+      D[row * N + n + r] = to_out_bits(v[r], bf16);
     }
   }
 }
@@ -509,6 +503,14 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
   // ---- epilogue: lane holds D[row, n .. n+3], row = block row r16
   const bool bf16 = p.out_bf16 != 0;
   const bool vec = p.d_vec4 != 0;
+  // this lane's bias columns, loaded once (the output stores could alias the
+  // bias, so the compiler would otherwise reload it before every store)
+  f32x4 bias4[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int64_t n = n0 + wn * TN + j * 16 + 4 * g;
+    bias4[j] = p.bias && n < N ? load_bias4(p.bias, n, N, bf16, vec && n + 3 < N) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int64_t slot = m_lo + wm * TM + i * 16 + r16;
@@ -522,7 +524,7 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
     for (int j = 0; j < FN; ++j) {
       const int64_t n = n0 + wn * TN + j * 16 + 4 * g;
       if (n >= N) continue;
-      store4(p, drow, n, acc[i][j], bf16, vec);
+      store4(p, drow, n, p.bias ? acc[i][j] + bias4[j] : acc[i][j], bf16, vec);
     }
   }
 }
@@ -816,7 +818,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_stream(TileParams p) {
 #pragma unroll
     for (int ww = 1; ww < NW; ++ww) sum += red[ww][mb][l2];
     const int64_t n = n0 + 4 * (l2 >> 4);
-    if (n < N) store4(p, m, n, sum, bf16, vec);
+    if (n < N) store4(p, m, n, p.bias ? sum + load_bias4(p.bias, n, N, bf16, vec && n + 3 < N) : sum, bf16, vec);
   }
 }
 

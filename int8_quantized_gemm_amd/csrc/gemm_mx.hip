@@ -78,23 +78,12 @@ __device__ __forceinline__ uint32_t out_bits(float v, bool bf16) {
   return bf16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
 }
 
-__device__ __forceinline__ float bias_at(const void* b, int64_t n, bool bf16) {
-  const uint16_t h = static_cast<const uint16_t*>(b)[n];
-  return bf16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
-}
-
-// D[row, n .. n+3] (+ bias) as 16-bit values
+// D[row, n .. n+3] as 16-bit values (any bias already added)
 __device__ __forceinline__ void store4_mx(const MxParams& p, int64_t row, int64_t n, f32x4 v,
                                           bool bf16, bool vec) {
   uint16_t* D = static_cast<uint16_t*>(p.D);
   const int64_t N = p.N;
   if (vec && n + 3 < N) {
-    if (p.bias) {
-      const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.bias) + n);
-      const uint32_t h[4] = {b.x & 0xFFFFu, b.x >> 16, b.y & 0xFFFFu, b.y >> 16};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] += bf16 ? bf16_bits_to_f32(h[r]) : f16_bits_to_f32(h[r]);
-    }
     uint2 o;
     o.x = out_bits(v[0], bf16) | (out_bits(v[1], bf16) << 16);
     o.y = out_bits(v[2], bf16) | (out_bits(v[3], bf16) << 16);
@@ -103,8 +92,7 @@ __device__ __forceinline__ void store4_mx(const MxParams& p, int64_t row, int64_
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (n + r >= N) break;
-      const float bv = p.bias ? bias_at(p.bias, n + r, bf16) : 0.0f;
-      D[row * N + n + r] = (uint16_t)out_bits(v[r] + bv, bf16);
+      D[row * N + n + r] = (uint16_t)out_bits(v[r], bf16);
     }
   }
 }
@@ -245,6 +233,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_mx(MxParams p) {
   }
 
   const bool bf16 = p.out_bf16 != 0, vec = p.d_vec4 != 0;
+  // this lane's bias columns, loaded once (the output stores could alias the
+  // bias, so the compiler would otherwise reload it before every store)
+  f32x4 bias4[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int64_t n = n0 + wn * TN + j * 16 + 4 * g;
+    bias4[j] = p.bias && n < N ? load_bias4(p.bias, n, N, bf16, vec && n + 3 < N) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int64_t row = m_lo + wm * TM + i * 16 + r16;
@@ -253,7 +249,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_mx(MxParams p) {
     for (int j = 0; j < FN; ++j) {
       const int64_t n = n0 + wn * TN + j * 16 + 4 * g;
       if (n >= N) continue;
-      store4_mx(p, row, n, acc[i][j], bf16, vec);
+      store4_mx(p, row, n, p.bias ? acc[i][j] + bias4[j] : acc[i][j], bf16, vec);
     }
   }
 }
@@ -327,7 +323,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_stream_mx(MxParams p) {
 #pragma unroll
     for (int ww = 1; ww < NW; ++ww) sum += red[ww][mb][l2];
     const int64_t n = n0 + 4 * (l2 >> 4);
-    if (n < N) store4_mx(p, m, n, sum, bf16, vec);
+    if (n < N) store4_mx(p, m, n, p.bias ? sum + load_bias4(p.bias, n, N, bf16, vec && n + 3 < N) : sum, bf16, vec);
   }
 }
 

@@ -290,12 +290,32 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_scaled_pipe(ScaledParams p)
     step(kt, kt + 1 < KT, odd ? sA0 : sA1, odd ? sB0 : sB1, odd ? sA1 : sA0, odd ? sB1 : sB0);
   }
 
-  // epilogue: lane holds D[m, n .. n+3]
+  // epilogue: lane holds D[m, n .. n+3]. The row scales, column scales and
+  // bias this lane needs are loaded once, up front (the output stores could
+  // alias them, so the compiler would otherwise reload them before every
+  // store, one round trip each).
+  const bool scaled = FP8 || p.out_kind != 0;
+  float sa_r[FM];
+  f32x4 sb4[FN], b4[FN];
+  if (scaled) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = m0 + wm * TM + i * 16 + r16;
+      sa_r[i] = m < M ? p.sa[p.sa_per_row ? m : 0] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = n0 + wn * TN + j * 16 + 4 * g;
+      const bool in = n < N;  // N % 16 == 0: n .. n+3 all in range otherwise
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sb4[j][r] = in ? p.sb[p.sb_per_col ? n + r : 0] : 0.0f;
+      b4[j] = p.bias && in ? load_bias4(p.bias, n, N, p.out_kind == 1, true) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int64_t m = m0 + wm * TM + i * 16 + r16;
     if (m >= M) continue;
-    const float sav = p.out_kind != 0 ? p.sa[p.sa_per_row ? m : 0] : 0.0f;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int64_t n = n0 + wn * TN + j * 16 + 4 * g;
@@ -307,12 +327,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_scaled_pipe(ScaledParams p)
         uint32_t o[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float sbv = p.sb[p.sb_per_col ? n + r : 0];
-          float f = __fmul_rn(__fmul_rn((float)v[r], sav), sbv);
-          if (p.bias) {
-            const uint16_t hb = static_cast<const uint16_t*>(p.bias)[n + r];
-            f = __fadd_rn(f, p.out_kind == 1 ? bf16_bits_to_f32(hb) : f16_bits_to_f32(hb));
-          }
+          float f = __fmul_rn(__fmul_rn((float)v[r], sa_r[i]), sb4[j][r]);
+          if (p.bias) f = __fadd_rn(f, b4[j][r]);
           o[r] = p.out_kind == 1 ? f32_to_bf16_bits(f) : f32_to_f16_bits(f);
         }
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.D) + m * N + n) =

@@ -50,6 +50,24 @@ __device__ __forceinline__ float out_bits_to_f32(uint32_t h) {
   else return f16_bits_to_f32(h);
 }
 
+// Four consecutive 16-bit bias values b[n .. n+3] as float32, zero past n_end.
+// vec: b + n is 8-byte aligned and n + 3 < n_end, one 8-byte load.
+__device__ __forceinline__ f32x4 load_bias4(const void* b, int64_t n, int64_t n_end, bool bf16, bool vec) {
+  const uint16_t* h = static_cast<const uint16_t*>(b);
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  if (vec) {
+    const uint2 w = *reinterpret_cast<const uint2*>(h + n);
+    const uint32_t u[4] = {w.x & 0xFFFFu, w.x >> 16, w.y & 0xFFFFu, w.y >> 16};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = bf16 ? bf16_bits_to_f32(u[r]) : f16_bits_to_f32(u[r]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < n_end) v[r] = bf16 ? bf16_bits_to_f32(h[n + r]) : f16_bits_to_f32(h[n + r]);
+  }
+  return v;
+}
+
 // ---- wave reductions ----------------------------------------------------------
 __device__ __forceinline__ float wave_max_xor(float v, int width) {
   for (int off = width >> 1; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
