@@ -503,28 +503,37 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
   // ---- epilogue: lane holds D[row, n .. n+3], row = block row r16
   const bool bf16 = p.out_bf16 != 0;
   const bool vec = p.d_vec4 != 0;
-  // this lane's bias columns, loaded once (the output stores could alias the
-  // bias, so the compiler would otherwise reload it before every store)
+  // Everything the stores need from memory is loaded once, up front: this
+  // lane's bias columns and (grouped) its output rows. The stores could alias
+  // these arrays, so loads left between them would each wait for every store
+  // before them to complete.
   f32x4 bias4[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int64_t n = n0 + wn * TN + j * 16 + 4 * g;
-    bias4[j] = p.bias && n < N ? load_bias4(p.bias, n, N, bf16, vec && n + 3 < N) : f32x4{0.f, 0.f, 0.f, 0.f};
+    bias4[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (!GROUPED) {  // the grouped entry point has no bias
+      if (p.bias && n < N) bias4[j] = load_bias4(p.bias, n, N, bf16, vec && n + 3 < N);
+    }
   }
+  int64_t drow[FM];  // output row of block row i, -1 for none
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int64_t slot = m_lo + wm * TM + i * 16 + r16;
-    if (slot >= m_hi) continue;
-    int64_t drow = slot;
+    drow[i] = slot < m_hi ? slot : -1;
     if constexpr (GROUPED) {
-      drow = p.c_inv ? (int64_t)p.c_inv[slot] : slot;
-      if (drow < 0 || drow >= p.M) continue;  // c_map was not a permutation
+      if (slot < m_hi && p.c_inv) drow[i] = p.c_inv[slot];
+      if (drow[i] >= p.M) drow[i] = -1;  // c_map was not a permutation
     }
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    if (drow[i] < 0) continue;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int64_t n = n0 + wn * TN + j * 16 + 4 * g;
       if (n >= N) continue;
-      store4(p, drow, n, p.bias ? acc[i][j] + bias4[j] : acc[i][j], bf16, vec);
+      store4(p, drow[i], n, GROUPED || !p.bias ? acc[i][j] : acc[i][j] + bias4[j], bf16, vec);
     }
   }
 }
