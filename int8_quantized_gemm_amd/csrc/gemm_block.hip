@@ -142,7 +142,7 @@ struct TileSmem {
 // sm holds stages of at least BM (A) and BN (W) rows; the activation-scale
 // stages, [KSUB][WM][FM/4][16][4], let a lane read its FM row-block scales as
 // FM/4 16-byte vectors, consecutive lanes 16 bytes apart (conflict free).
-template <int BM, int BN, int WM, int WN, int KS, bool GROUPED, bool WSU>
+template <int BM, int BN, int WM, int WN, int KS, bool GROUPED, bool WSU, bool BIAS>
 __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int64_t m_hi, int64_t n0,
                                           int e, const TileSmem& sm) {
   constexpr int NW = WM * WN;
@@ -504,16 +504,18 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
   const bool bf16 = p.out_bf16 != 0;
   const bool vec = p.d_vec4 != 0;
   // Everything the stores need from memory is loaded once, up front: this
-  // lane's bias columns and (grouped) its output rows. The stores could alias
-  // these arrays, so loads left between them would each wait for every store
-  // before them to complete.
+  // lane's bias columns (an instance of its own, so the kernel without a bias
+  // carries none of this) and, grouped, its output rows. The stores could
+  // alias these arrays, so loads left between them would each wait for every
+  // store before them to complete.
+  static_assert(!(GROUPED && BIAS), "the grouped entry point has no bias");
   f32x4 bias4[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int64_t n = n0 + wn * TN + j * 16 + 4 * g;
     bias4[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (!GROUPED) {  // the grouped entry point has no bias
-      if (p.bias && n < N) bias4[j] = load_bias4(p.bias, n, N, bf16, vec && n + 3 < N);
+    if constexpr (BIAS) {
+      if (n < N) bias4[j] = load_bias4(p.bias, n, N, bf16, vec && n + 3 < N);
     }
   }
   int64_t drow[FM];  // output row of block row i, -1 for none
@@ -533,7 +535,7 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
     for (int j = 0; j < FN; ++j) {
       const int64_t n = n0 + wn * TN + j * 16 + 4 * g;
       if (n >= N) continue;
-      store4(p, drow[i], n, GROUPED || !p.bias ? acc[i][j] : acc[i][j] + bias4[j], bf16, vec);
+      store4(p, drow[i], n, BIAS ? acc[i][j] + bias4[j] : acc[i][j], bf16, vec);
     }
   }
 }
@@ -549,7 +551,7 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
 
 // One tile shape over the whole output (dense), or over the experts' row
 // ranges (GROUPED).
-template <int BM, int BN, int WM, int WN, int KS, bool GROUPED, bool WSU>
+template <int BM, int BN, int WM, int WN, int KS, bool GROUPED, bool WSU, bool BIAS>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
   Q8_TILE_SMEM(BM, BN, 128 / KS);
   const int lane = threadIdx.x & 63;
@@ -610,7 +612,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
     m_hi = m_lo + BM < p.M ? m_lo + BM : p.M;
     n0 = tn * BN;
   }
-  tile_body<BM, BN, WM, WN, KS, GROUPED, WSU>(p, m_lo, m_hi, n0, e, sm);
+  tile_body<BM, BN, WM, WN, KS, GROUPED, WSU, BIAS>(p, m_lo, m_hi, n0, e, sm);
 }
 
 // ------------------------------------------------------------------------------
@@ -1057,10 +1059,17 @@ hipError_t launch_tile(const TileParams& tp, int64_t tiles, hipStream_t st) {
   // wave's column range never crosses a bn boundary
   const bool wsu = tp.bn % TN == 0;
   const dim3 grid((unsigned)tiles), block(kWM * kWN * 64);
-  if (wsu)
-    hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED, true>), grid, block, 0, st, tp);
-  else
-    hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED, false>), grid, block, 0, st, tp);
+  if (!GROUPED && tp.bias) {
+    constexpr bool B = !GROUPED;
+    if (wsu)
+      hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED, true, B>), grid, block, 0, st, tp);
+    else
+      hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED, false, B>), grid, block, 0, st, tp);
+  } else if (wsu) {
+    hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED, true, false>), grid, block, 0, st, tp);
+  } else {
+    hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED, false, false>), grid, block, 0, st, tp);
+  }
   return hipGetLastError();
 }
 
