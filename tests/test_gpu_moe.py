@@ -156,7 +156,9 @@ def finalize_bound(w, D_rows, ref):
 
 @pytest.mark.parametrize("T,topk,N,dtype,perm,weights", [
     (4096, 8, 2048, "bf16", True, True), (4096, 8, 2048, "bf16", False, True),
-    (37, 3, 100, "f16", True, True), (5, 2, 24, "bf16", False, False), (70000, 1, 16, "bf16", True, True)])
+    (37, 3, 100, "f16", True, True), (5, 2, 24, "bf16", False, False), (70000, 1, 16, "bf16", True, True),
+    # more than one batch of eight rows per token, full and partial
+    (50, 10, 264, "bf16", True, True), (33, 16, 2048, "bf16", True, True), (21, 9, 100, "f16", False, True)])
 def test_finalize_parity(T, topk, N, dtype, perm, weights):
     """Synthetic routed rows and gate weights on both sides; with ``perm`` the
     rows are in expert-sorted order and the routing table names them."""
