@@ -104,6 +104,16 @@ def test_tile_k_extent(M, N, K):
     run_case(M, N, K, 128, 128, bias=True, seed=K)
 
 
+@pytest.mark.parametrize("M,N,K,bn,bk,out_dtype", [
+    (130, 301, 1024, 128, 128, torch.bfloat16), (70, 517, 512, 32, 32, torch.bfloat16),
+    (200, 603, 512, 48, 128, torch.bfloat16), (130, 301, 1024, 128, 128, torch.float16)])
+def test_bias_unaligned_columns(M, N, K, bn, bk, out_dtype):
+    """A bias with N not a multiple of four: the tile kernel's bias instance
+    then reads and stores element by element (and with bn = 48 takes the
+    general slab loop)."""
+    run_case(M, N, K, bn, bk, ue=(bk == 32), bias=True, out_dtype=out_dtype, seed=N)
+
+
 @pytest.mark.parametrize("bn", [48, 64, 256])
 def test_weight_block_rows_differ_from_bk(bn):
     run_case(200, 600, 512, bn, 128, seed=3)
