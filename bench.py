@@ -516,11 +516,11 @@ class _Null:
 
 
 def traffic_probe(torch, q8, synth) -> int:
-    """Kernels for the HBM byte counters: three prefill GEMM launches and three
-    decode GEMM launches at M=1 and at M=16 (a 256 MiB fill before each, so the
-    operands are not resident in the Infinity Cache), and three plain 256 MiB
-    device-to-device copies of known size (the scale for FETCH_SIZE /
-    WRITE_SIZE)."""
+    """Kernels for the HBM byte counters: three prefill GEMM launches, three
+    decode GEMM launches at M=1 and at M=16, and three MoE grouped GEMM
+    launches (a 256 MiB fill before each, so the operands are not resident in
+    the Infinity Cache), and three plain 256 MiB device-to-device copies of
+    known size (the scale for FETCH_SIZE / WRITE_SIZE)."""
     M, N, K, blk = 4096, 7168, 7168, 128
     dev = "cuda:0"
     x = synth.activations(M, K, "bf16", seed=0).to(dev)
@@ -550,11 +550,29 @@ def traffic_probe(torch, q8, synth) -> int:
             q8.quant_8bit(xd, aqd, Asd, db, EPS, -448.0, 448.0, True)
             big.fill_(1)
             q8.blockwise_scaled_mm(aqd, Wd, Asd, Wsd, torch.bfloat16, block=(db, db), out=Dd)
+    # MoE grouped GEMM (4096 tokens, top-8 of 64 experts, N=2048, K=7168) with
+    # the fused gather and scatter: 939.5 MB of expert weights per launch
+    del Wq, Ws, D, Wd, Wsd
+    T, E, topk, Ne = 4096, 64, 8, 2048
+    ids = synth.zipf_topk_ids(T, E, topk, seed=0).to(dev)
+    We, Wse = synth.fp8_block_weights(Ne, K, blk, blk, experts=E, seed=0)
+    We, Wse = We.to(dev), Wse.to(dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    ps1 = torch.empty((E, 3), dtype=torch.int32, device=dev)
+    ps2 = torch.empty((E, 3), dtype=torch.int32, device=dev)
+    ip = torch.empty(T * topk, dtype=torch.int32, device=dev)
+    op = torch.empty(T * topk, dtype=torch.int32, device=dev)
+    De = torch.empty((T * topk, Ne), dtype=torch.bfloat16, device=dev)
+    q8.moe_mm_data(ids, off, ps1, ps2, ip, op, E, Ne, K)
+    q8.quant_8bit(x, aq, As, blk, EPS, -448.0, 448.0, False)
+    for _ in range(3):
+        big.fill_(1)
+        q8.grouped_blockwise_scaled_mm(De, aq, We, As, Wse, off, ps1, a_map=ip, c_map=op)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
     log("traffic probe done: 3 prefill GEMM launches, 3 decode GEMM launches each at M=1 and M=16, "
-        "3 copies of 268435456 bytes")
+        "3 MoE grouped GEMM launches, 3 copies of 268435456 bytes")
     return 0
 
 
