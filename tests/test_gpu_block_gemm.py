@@ -82,6 +82,16 @@ def test_decode_shared_activation_shapes(M, N, K, bk):
     run_case(M, N, K, bk, bk, ue=(bk == 32), bias=True, seed=M * 7 + K)
 
 
+@pytest.mark.parametrize("M,N,K,bn,bk", [(17, 1000, 1024, 128, 128), (33, 4096, 7168, 32, 32),
+                                        (48, 520, 2048, 32, 32), (64, 300, 512, 128, 128),
+                                        (40, 4096, 7168, 128, 128), (30, 600, 1024, 48, 128)])
+def test_decode_mid_rows(M, N, K, bn, bk):
+    """17 .. 64 activation rows (two to four 16-row activation blocks per
+    wave in the streaming kernel): ragged N, bias, fewer K chunks than waves,
+    bn != bk."""
+    run_case(M, N, K, bn, bk, ue=(bk == 32), bias=True, seed=M + N)
+
+
 @pytest.mark.parametrize("N", [7168, 18432])
 @pytest.mark.parametrize("bias", [False, True])
 def test_prefill_full_size_sampled_rows(N, bias):
