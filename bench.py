@@ -614,7 +614,7 @@ def main() -> int:
     ap.add_argument("--skip-secondary", action="store_true", help="headline prefill only")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         return 2
 

@@ -36,7 +36,7 @@ enum {
   Q8_OK = 0,
   Q8_EINVAL = -1,        /* null pointer, bad dtype or enum value          */
   Q8_ESHAPE = -2,        /* a size or divisibility rule is broken          */
-  Q8_EUNSUPPORTED = -3,  /* a valid request this build does not implement  */
+  Q8_EUNSUPPORTED = -3,  /* a valid request the library does not implement */
   Q8_EWORKSPACE = -4,    /* workspace missing or smaller than required     */
   Q8_EHIP = -5           /* a HIP call (kernel launch) failed              */
 };
