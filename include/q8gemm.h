@@ -7,8 +7,10 @@
  * - Every pointer argument is a DEVICE pointer (hipMalloc'd or a torch CUDA
  *   tensor's data_ptr), unless a comment says otherwise. The caller owns and
  *   allocates every buffer, outputs and workspace included; outputs are
- *   written in place. The library never allocates or frees memory, keeps no
- *   global state and may be called from several threads at once.
+ *   written in place. The library never allocates or frees memory and may be
+ *   called from several threads at once. Its only process-wide state is a
+ *   per-device record that a kernel's LDS limit was raised (set once,
+ *   thread-safe).
  * - Every matrix is row-major and contiguous unless a leading dimension is
  *   passed. Weights are [N, K] with K contiguous (the "nt" layout: a
  *   column-major [K, N] weight is the same bytes).
@@ -272,7 +274,7 @@ int grouped_blockwise_scaled_mm(const void* A, const float* As, const void* W, c
  * MoE finalize: weight every routed row by its top-k gate weight and sum each
  * token's top-k rows.
  * "Implementation: Sgl project Sglang Fused MoE Marlin", I/O Contract:
- * topk_weights ("Top-k routing weights from MoE gate"), mul_topk_weights
+ * topk_weights (the router's gate weight of each chosen expert), mul_topk_weights
  * (multiply the output by them) and the reduction of the routed outputs
  * (use_atomic_add, use_fp32_reduce). Here the reduction is deterministic.
  *

@@ -135,6 +135,29 @@ def _contig(*ts) -> None:
             raise ValueError("tensor must be contiguous")
 
 
+def _need(cond: bool, msg: str) -> None:
+    """Host-side argument check: raised before any device work, so a tensor
+    too small for what the kernels write or read is never handed to them."""
+    if not cond:
+        raise ValueError(msg)
+
+
+_FP8 = (torch.float8_e4m3fn, torch.uint8)
+_OUT16 = (torch.bfloat16, torch.float16)
+_BYTE_SCALE = tuple(t for t in (torch.uint8, getattr(torch, "float8_e8m0fnu", None)) if t is not None)
+
+
+def _check_bias(bias, N: int, out_dtype) -> None:
+    if bias is not None:
+        _need(bias.dtype == out_dtype, f"bias dtype {bias.dtype} must be the output dtype {out_dtype}")
+        _need(bias.numel() == N, f"bias must have N = {N} elements (has {bias.numel()})")
+
+
+def _check_out(out, M: int, N: int, dtypes) -> None:
+    _need(tuple(out.shape) == (M, N), f"out must be [{M}, {N}] (is {list(out.shape)})")
+    _need(out.dtype in dtypes, f"out dtype {out.dtype} not supported")
+
+
 def _stream(dev: int) -> int:
     """Raw handle of torch's current stream on device ``dev`` (no Stream object)."""
     return torch._C._cuda_getCurrentRawStream(dev)
@@ -188,7 +211,6 @@ def quant_8bit(input: torch.Tensor, output_q: torch.Tensor, output_s: torch.Tens
     3-D [E, max_m, .] and only the first ``masked_m[e]`` rows of block ``e``
     are quantized; the other rows of the outputs are left as they were.
     """
-    dev = _dev(input, output_q, output_s, masked_m)
     max_m = 0
     if masked_m is not None:
         if input.dim() != 3 or masked_m.dtype != torch.int32 or masked_m.numel() != input.shape[0]:
@@ -210,10 +232,25 @@ def quant_8bit(input: torch.Tensor, output_q: torch.Tensor, output_s: torch.Tens
         raise ValueError("fuse_silu_and_mul needs an even input width")
     if tuple(output_q.shape) != (M, K):
         raise ValueError("output_q must be [M, K] (K = half the input width when fused)")
+    _need(input.dtype in (torch.float32, torch.bfloat16, torch.float16), "input must be fp32, bf16 or f16")
+    _need(output_q.dtype in _FP8 + (torch.int8,), "output_q must be float8_e4m3fn, uint8 or int8")
+    ue = int(scale_ue8m0)
+    if ue == 2:
+        _need(output_s.dtype in _BYTE_SCALE, "scale_ue8m0=2 stores one E8M0 byte per scale (uint8)")
+    else:
+        _need(output_s.dtype == torch.float32, "output_s must be float32")
+    if mode == SCALE_PER_GROUP:
+        if group_size >= 1 and K % group_size == 0:
+            _need(output_s.numel() == M * (K // group_size),
+                  f"output_s must hold M * K / group_size = {M * (K // group_size)} scales "
+                  f"(has {output_s.numel()})")
+    else:
+        _need(output_s.numel() == 1, "per-tensor modes take a one-element output_s")
+    dev = _dev(input, output_q, output_s, masked_m)
     ws, wsb = _workspace(dev, _ws_size(_quant_ws, M, K, mode))
     _check(_quant(_ptr(input), _dt(input.dtype), M, K, input.stride(0) if M > 1 else Kin,
                   _ptr(output_q), _dt(output_q.dtype), _ptr(output_s), group_size, mode, eps,
-                  fp8_min, fp8_max, int(scale_ue8m0), int(fuse_silu_and_mul), _ptr(masked_m),
+                  fp8_min, fp8_max, ue, int(fuse_silu_and_mul), _ptr(masked_m),
                   max_m, ws, wsb, _stream(dev)))
 
 
@@ -223,13 +260,22 @@ def blockwise_scaled_mm(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torc
                         out: torch.Tensor | None = None) -> torch.Tensor:
     """Block-scaled FP8 GEMM ``D = A @ W.T`` with per-(row, K block) ``scales_a``
     [M, K/bk] and per-(bn x bk tile) ``scales_b`` [ceil(N/bn), K/bk]."""
-    dev = _dev(mat_a, mat_b, scales_a, scales_b, bias, out)
     _contig(mat_a, mat_b, scales_a, scales_b, bias)
     M, K = mat_a.shape
     N = mat_b.shape[0]
     if mat_b.shape[1] != K:
         raise ValueError("mat_b must be [N, K]")
     bn, bk = block
+    _need(mat_a.dtype in _FP8 and mat_b.dtype in _FP8, "mat_a and mat_b must be float8_e4m3fn (or uint8 codes)")
+    _need(scales_a.dtype == torch.float32 and scales_b.dtype == torch.float32, "scales must be float32")
+    if bk >= 1 and bn >= 1 and K % bk == 0:
+        _need(scales_a.numel() == M * (K // bk), f"scales_a must be [M, K/bk] = [{M}, {K // bk}]")
+        _need(scales_b.numel() == -(-N // bn) * (K // bk),
+              f"scales_b must be [ceil(N/bn), K/bk] = [{-(-N // bn)}, {K // bk}]")
+    _check_bias(bias, N, out.dtype if out is not None else out_dtype)
+    if out is not None:
+        _check_out(out, M, N, _OUT16)
+    dev = _dev(mat_a, mat_b, scales_a, scales_b, bias, out)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=dev)
     _contig(out)
@@ -246,7 +292,6 @@ def blockwise_scaled_mm_e8m0(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a:
     """Block-scaled FP8 GEMM with E8M0 (power-of-two) scales on both operands:
     ``scales_a`` [M, K/32] and ``scales_b`` [ceil(N/block_n), K/32] as uint8
     (or torch.float8_e8m0fnu) bytes, 32-wide K blocks."""
-    dev = _dev(mat_a, mat_b, scales_a, scales_b, bias, out)
     _contig(mat_a, mat_b, scales_a, scales_b, bias)
     M, K = mat_a.shape
     N = mat_b.shape[0]
@@ -255,6 +300,15 @@ def blockwise_scaled_mm_e8m0(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a:
     for t in (scales_a, scales_b):
         if t.element_size() != 1:
             raise ValueError("E8M0 scales are one byte each")
+    _need(mat_a.dtype in _FP8 and mat_b.dtype in _FP8, "mat_a and mat_b must be float8_e4m3fn (or uint8 codes)")
+    if K % 32 == 0 and block_n >= 1:
+        _need(scales_a.numel() == M * (K // 32), f"scales_a must be [M, K/32] = [{M}, {K // 32}]")
+        _need(scales_b.numel() == -(-N // block_n) * (K // 32),
+              f"scales_b must be [ceil(N/block_n), K/32] = [{-(-N // block_n)}, {K // 32}]")
+    _check_bias(bias, N, out.dtype if out is not None else out_dtype)
+    if out is not None:
+        _check_out(out, M, N, _OUT16)
+    dev = _dev(mat_a, mat_b, scales_a, scales_b, bias, out)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=dev)
     _contig(out)
@@ -268,8 +322,10 @@ def scaled_mm_int8(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torch.Ten
                    bias: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
     """INT8 W8A8: ``mat_a`` [M, K] int8; ``mat_b`` [N, K] int8 (or its ``.t()``
     view [K, N]); ``out_dtype=torch.int32`` returns the raw accumulators."""
-    dev = _dev(mat_a, mat_b, scales_a, scales_b, bias, out)
     _contig(mat_a, scales_a, scales_b, bias)
+    _need(mat_a.dtype == torch.int8 and mat_b.dtype == torch.int8, "mat_a and mat_b must be int8")
+    for t in (scales_a, scales_b):
+        _need(t is None or t.dtype == torch.float32, "scales must be float32")
     M, K = mat_a.shape
     if mat_b.is_contiguous() and mat_b.shape[1] == K:
         N = mat_b.shape[0]
@@ -277,6 +333,10 @@ def scaled_mm_int8(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torch.Ten
         N = mat_b.shape[1]  # transposed view of a contiguous [N, K]
     else:
         raise ValueError("mat_b must be [N, K] contiguous or the .t() view of one")
+    _check_bias(bias, N, out.dtype if out is not None else out_dtype)
+    if out is not None:
+        _check_out(out, M, N, _OUT16 + (torch.int32,))
+    dev = _dev(mat_a, mat_b, scales_a, scales_b, bias, out)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=dev)
     _contig(out)
@@ -292,8 +352,9 @@ def scaled_mm_fp8(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torch.Tens
     """FP8 per-tensor / per-token x per-channel: ``mat_a`` [M, K] e4m3fn;
     ``mat_b`` [N, K] e4m3fn (or its ``.t()`` view [K, N]); ``scales_a`` numel 1
     or M, ``scales_b`` numel 1 or N (float32)."""
-    dev = _dev(mat_a, mat_b, scales_a, scales_b, bias, out)
     _contig(mat_a, scales_a, scales_b, bias)
+    _need(mat_a.dtype in _FP8 and mat_b.dtype in _FP8, "mat_a and mat_b must be float8_e4m3fn (or uint8 codes)")
+    _need(scales_a.dtype == torch.float32 and scales_b.dtype == torch.float32, "scales must be float32")
     M, K = mat_a.shape
     if mat_b.is_contiguous() and mat_b.shape[1] == K:
         N = mat_b.shape[0]
@@ -301,6 +362,10 @@ def scaled_mm_fp8(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torch.Tens
         N = mat_b.shape[1]  # transposed view of a contiguous [N, K]
     else:
         raise ValueError("mat_b must be [N, K] contiguous or the .t() view of one")
+    _check_bias(bias, N, out.dtype if out is not None else out_dtype)
+    if out is not None:
+        _check_out(out, M, N, _OUT16)
+    dev = _dev(mat_a, mat_b, scales_a, scales_b, bias, out)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=dev)
     _contig(out)
@@ -314,8 +379,6 @@ def moe_mm_data(topk_ids: torch.Tensor, expert_offsets: torch.Tensor,
                 input_permutation: torch.Tensor, output_permutation: torch.Tensor,
                 num_experts: int, n: int, k: int) -> None:
     """MoE routing tables from ``topk_ids`` [T, topk] int32, in place."""
-    dev = _dev(topk_ids, expert_offsets, problem_sizes1, problem_sizes2, input_permutation,
-               output_permutation)
     _contig(topk_ids, expert_offsets, problem_sizes1, problem_sizes2, input_permutation,
             output_permutation)
     for t in (topk_ids, expert_offsets, problem_sizes1, problem_sizes2, input_permutation,
@@ -327,6 +390,8 @@ def moe_mm_data(topk_ids: torch.Tensor, expert_offsets: torch.Tensor,
             or problem_sizes2.numel() < 3 * num_experts \
             or input_permutation.numel() < T * topk or output_permutation.numel() < T * topk:
         raise ValueError("an output tensor is too small")
+    dev = _dev(topk_ids, expert_offsets, problem_sizes1, problem_sizes2, input_permutation,
+               output_permutation)
     ws, wsb = _workspace(dev, _moe_ws(T, topk, num_experts))
     _check(_moe(_ptr(topk_ids), T, topk, num_experts, n, k, _ptr(expert_offsets),
                 _ptr(problem_sizes1), _ptr(problem_sizes2), _ptr(input_permutation),
@@ -341,7 +406,6 @@ def moe_finalize(d: torch.Tensor, topk_weights: torch.Tensor | None, topk: int,
     ``d`` [T*topk, N] bf16/f16, un-permuted, or expert-sorted with
     ``output_permutation`` (int32 [T*topk]) naming the row of each choice.
     """
-    dev = _dev(d, topk_weights, output_permutation, out)
     _contig(d, topk_weights, output_permutation)
     rows, N = d.shape
     if rows % topk:
@@ -352,6 +416,10 @@ def moe_finalize(d: torch.Tensor, topk_weights: torch.Tensor | None, topk: int,
     if output_permutation is not None and (output_permutation.dtype != torch.int32
                                            or output_permutation.numel() != rows):
         raise ValueError("output_permutation must be int32 [T * topk]")
+    _need(d.dtype in _OUT16, "d must be bf16 or f16")
+    if out is not None:
+        _check_out(out, T, N, (d.dtype,))
+    dev = _dev(d, topk_weights, output_permutation, out)
     if out is None:
         out = torch.empty((T, N), dtype=d.dtype, device=dev)
     _contig(out)
@@ -371,13 +439,32 @@ def grouped_blockwise_scaled_mm(d: torch.Tensor, a: torch.Tensor, b: torch.Tenso
     rows are addressed through ``a_map`` (input_permutation) when given;
     ``c_map`` (output_permutation) un-permutes the result rows.
     """
-    dev = _dev(d, a, b, a_scales, b_scales, expert_offsets, problem_sizes, a_map, c_map)
     _contig(d, a, b, a_scales, b_scales, expert_offsets, problem_sizes, a_map, c_map)
     E, N, K = b.shape
     total_m = d.shape[0]
     if d.shape[1] != N or a.shape[1] != K:
         raise ValueError("shape mismatch")
     bn, bk = block
+    _need(a.dtype in _FP8 and b.dtype in _FP8, "a and b must be float8_e4m3fn (or uint8 codes)")
+    _need(d.dtype in _OUT16, "d must be bf16 or f16")
+    _need(a_scales.dtype == torch.float32 and b_scales.dtype == torch.float32, "scales must be float32")
+    for t, name in ((expert_offsets, "expert_offsets"), (problem_sizes, "problem_sizes"),
+                    (a_map, "a_map"), (c_map, "c_map")):
+        _need(t is None or t.dtype == torch.int32, f"{name} must be int32")
+    _need(expert_offsets.numel() == E + 1, f"expert_offsets must have E + 1 = {E + 1} entries")
+    _need(problem_sizes.numel() == 3 * E, f"problem_sizes must be [E, 3] = [{E}, 3]")
+    if bk >= 1 and K % bk == 0 and bn >= 1:
+        _need(a_scales.dim() == 2 and tuple(a_scales.shape) == (a.shape[0], K // bk),
+              f"a_scales must be [rows of a, K/bk] = [{a.shape[0]}, {K // bk}]")
+        _need(b_scales.numel() == E * -(-N // bn) * (K // bk),
+              f"b_scales must be [E, ceil(N/bn), K/bk] = [{E}, {-(-N // bn)}, {K // bk}]")
+    if a_map is not None:
+        _need(a_map.numel() == total_m, f"a_map must have total_m = {total_m} entries")
+    else:
+        _need(a.shape[0] >= total_m, "without a_map, a must hold total_m sorted rows")
+    if c_map is not None:
+        _need(c_map.numel() == total_m, f"c_map must have total_m = {total_m} entries")
+    dev = _dev(d, a, b, a_scales, b_scales, expert_offsets, problem_sizes, a_map, c_map)
     ws, wsb = _workspace(dev, _gmm_ws(E, total_m, N, K, bn, bk) if c_map is not None else 0)
     _check(_gmm(_ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales), _ptr(d), _dt(d.dtype),
                 _ptr(expert_offsets), _ptr(problem_sizes), _ptr(a_map), _ptr(c_map), E, total_m,

@@ -25,6 +25,7 @@
 //             slot, so a lane's four outputs share one activation row and
 //             one scale product), and the waves' float32 partials are summed
 //             in a fixed order through LDS (deterministic).
+#include <atomic>
 #include <type_traits>
 
 #include "q8_internal.h"
@@ -1023,16 +1024,27 @@ inline bool stream_sa_fits(int64_t M, int64_t K, int KB) {
          stream_sa_lds(M, K, KB) <= kLdsBytes;
 }
 
+// Raises a kernel's dynamic-LDS limit to the whole 160 KB on the current
+// device, once per (kernel, device): `done` holds one bit per device. Threads
+// racing on a first call may both make the (idempotent) attribute call; the
+// bit is set only after it succeeded. Devices past the 64th set it every call.
+hipError_t raise_lds_limit(const void* kern, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? 1ull << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
+
 template <int KS>
 hipError_t launch_stream_sa(const TileParams& tp, hipStream_t st) {
   const auto kern = gemm_stream_sa<KS, kStreamSaNW, kStreamSaR>;
-  static bool attr_set = false;  // raising the limit is idempotent
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_raised{0};
+  const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kern), lds_raised);
+  if (e != hipSuccess) return e;
   if ((tp.N + 15) / 16 > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   const unsigned lds = (unsigned)stream_sa_lds(tp.M, tp.K, tp.KB);
   hipLaunchKernelGGL(kern, dim3((unsigned)((tp.N + 15) / 16)), dim3(kStreamSaNW * 64), lds, st, tp);

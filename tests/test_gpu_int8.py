@@ -63,14 +63,54 @@ def run_case(M, N, K, per_tensor, bias=True, rows=None, seed=0, transposed_b=Fal
     assert_gemm_close(d.cpu()[sel] if rows is not None else d, ref, f"int8 M={M} N={N} K={K}")
 
 
-def sample_rows(M, n=64, seed=0):
-    r = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, M - 1], r.choice(M, size=n, replace=False)]))
-
-
 @pytest.mark.parametrize("per_tensor", [False, True])
-def test_full_size_sampled_rows(per_tensor):
-    run_case(2048, 8192, 8192, per_tensor, rows=sample_rows(2048))
+def test_full_size_every_element(per_tensor):
+    """2048 x 8192 x 8192 as the benchmark launches it: every code, scale and
+    int32 accumulator bit for bit, every bf16 output within tolerance."""
+    run_case(2048, 8192, 8192, per_tensor)
+
+
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_ties_round_half_to_even(x_dtype, per_tensor):
+    """Quotients exactly halfway between two integers. Per token, rows whose
+    |max| is 127 get s = 1 and hold k + 0.5, rows whose |max| is 254 get s = 2
+    and hold odd integers (x / s = k + 0.5 again). Per tensor every row holds
+    odd integers and the |max| 254 sits in the last row (s = 2 for all).
+    Codes must be rint with ties to even, as the oracle has them and as
+    written out here from the values."""
+    M, K = 64, 1024
+    r = np.random.default_rng(11)
+    x = np.empty((M, K), dtype=np.float32)
+    for m in range(M):
+        if m % 2 == 0 and not per_tensor:
+            x[m] = r.integers(-127, 127, size=K) + 0.5    # all in (-127, 127)
+            x[m, r.integers(K)] = 127.0 if m % 4 == 0 else -127.0
+        else:
+            x[m] = 2 * r.integers(-127, 126, size=K) + 1  # odd, |x| <= 253
+            if not per_tensor:
+                x[m, r.integers(K)] = 254.0 if m % 4 == 1 else -254.0
+    if per_tensor:
+        x[M - 1, K // 2] = -254.0
+    xt = torch.from_numpy(x).to(torch.bfloat16 if x_dtype == "bf16" else torch.float32)
+    assert np.array_equal(xt.float().numpy(), x)          # every value exact in bf16
+    q, s = gpu_quant_int8(xt.to(DEV), per_tensor)
+    sync()
+    qo, so = oracle_quant_int8(xt, per_tensor)
+    assert np.array_equal(codes(q), qo)
+    assert np.array_equal(s.cpu().numpy().reshape(-1), so.reshape(-1))
+    if per_tensor:
+        scale = np.full((M, 1), 2.0)
+    else:
+        scale = np.where(np.arange(M) % 2 == 0, 1.0, 2.0)[:, None]
+    assert np.array_equal(so.reshape(-1), np.full(1, 2.0) if per_tensor else scale.reshape(-1))
+    y = x.astype(np.float64) / scale                      # exact: k + 0.5 or +-127
+    halves = y - np.floor(y) == 0.5
+    assert halves.mean() > 0.99
+    lo = np.floor(y)
+    even = np.where(lo % 2 == 0, lo, lo + 1)
+    expect = np.where(halves, even, y).astype(np.int64)
+    assert np.array_equal(codes(q).astype(np.int64), expect)
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 16), (5, 48, 1040), (300, 528, 1040), (257, 4096, 2048)])

@@ -96,19 +96,17 @@ def test_decode_size(M):
     assert_gemm_close(d, ref, f"decode M={M}")
 
 
-def test_prefill_size_sampled_rows():
+def test_prefill_size_every_element():
     """4096 x 7168 x 7168 with [32,32] power-of-two blocks, the launch the
-    benchmark times; the oracle computes 48 sampled rows."""
+    benchmark times: every output element."""
     M, N, K = 4096, 7168, 7168
     x, aq, asb = _act(M, K, seed=0)
     Wq, Wsb = synth.fp8_block_weights_e8m0(N, K, 32, 32, seed=0)
     d = q8().blockwise_scaled_mm_e8m0(torch.from_numpy(aq).to(DEV), Wq.to(DEV),
                                       torch.from_numpy(asb).to(DEV), Wsb.to(DEV), block_n=32)
     sync()
-    rows = np.random.default_rng(0).choice(M, 48, replace=False)
-    rows[:4] = [0, 255, 256, M - 1]
-    ref = og.blockwise_scaled_mm_e8m0(aq[rows], asb[rows], Wq.numpy(), Wsb.numpy(), 32)
-    assert_gemm_close(d[torch.from_numpy(rows).to(DEV)], ref, "prefill e8m0 sampled rows")
+    ref = og.blockwise_scaled_mm_e8m0(aq, asb, Wq.numpy(), Wsb.numpy(), 32)
+    assert_gemm_close(d, ref, "prefill e8m0")
 
 
 def test_quant_then_gemm_pipeline():

@@ -152,3 +152,49 @@ def test_static_scale():
 def test_rejects_ragged_group():
     with pytest.raises(ValueError):
         q8(np.zeros((1, 100), dtype=F32), 32)
+
+
+# ---- per-tensor dynamic scale over several rows -------------------------------
+# The expected codes below are written out by hand from the e4m3fn layout
+# (value (-1)^s (1 + m/8) 2^(e-7), code = s<<7 | e<<3 | m) and from rint with
+# ties to even: they do not come from the oracle. In every case the global
+# |max| sits in a later row than rows whose own maximum is smaller, so a scale
+# taken per row instead of over the whole tensor changes the codes of the
+# earlier rows and fails the pin.
+
+def test_per_tensor_dynamic_takes_the_max_over_all_rows():
+    x = np.array([[1.0, 2.0, 4.0, -8.0],
+                  [0.5, -16.0, 64.0, 3.0],
+                  [1792.0, -0.25, 6.0, 0.0]], dtype=F32)
+    q, s = quant.per_tensor_dynamic(x, EPS, -448.0, 448.0)
+    # |max| = 1792 = 448 * 4 in the last row: s = 4 exactly, codes of x / 4
+    assert s.shape == (1,) and s[0] == 4.0
+    # x/4:   0.25  0.5   1     -2   | 0.125  -4    16    0.75 | 448   -0.0625 1.5  0
+    expect = [[0x28, 0x30, 0x38, 0xC0], [0x20, 0xC8, 0x58, 0x34], [0x7E, 0x98, 0x3C, 0x00]]
+    assert q.tolist() == expect
+    # a per-row scale would have mapped row 0's maximum (8) to 448
+    assert q[0, 3] != 0xFE
+
+
+def test_per_tensor_dynamic_ue8m0_across_rows():
+    x = np.array([[100.0, -3.0, 2.0, 0.5],
+                  [1000.0, 12.0, -40.0, 1.0]], dtype=F32)
+    q, s = quant.per_tensor_dynamic(x, EPS, -448.0, 448.0, True)
+    # 1000 / 448 = 2.23.. rounds up to the power of two 4
+    assert s[0] == 4.0
+    # x/4: 25 (1.5625*16: mantissa 4.5 ties to even 4 -> 24), -0.75, 0.5, 0.125 |
+    #      250 (1.953*128 rounds up to 256 = 2^8: e=15, m=0), 3, -10, 0.25
+    expect = [[0x5C, 0xB4, 0x30, 0x20], [0x78, 0x44, 0xD2, 0x28]]
+    assert q.tolist() == expect
+
+
+def test_per_tensor_dynamic_int8_across_rows_and_ties():
+    x = np.array([[1.0, 3.0, 5.0, -7.0],
+                  [-1.0, -3.0, 9.0, 0.0],
+                  [254.0, 2.5, -5.0, 100.0]], dtype=F32)
+    q, s = quant.per_tensor_dynamic(x, EPS, -128.0, 127.0, False, "i8")
+    # |max| 254 in the last row: s = 254 / 127 = 2; x/2 = k + 0.5 rounds to even
+    assert s[0] == 2.0
+    assert q.tolist() == [[0, 2, 2, -4], [0, -2, 4, 0], [127, 1, -2, 50]]
+    # per row, row 0 would have had s = 7/127 and codes up to -127
+    assert q[0, 3] != -127
