@@ -239,6 +239,29 @@ int moe_mm_data(const int32_t* topk_ids, int64_t T, int topk, int E, int64_t n, 
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_mm_data without a workspace, for callers that cannot allocate device
+ * memory around the call: code under HIP graph capture, serving loops that
+ * must not allocate per step, harnesses that forbid hipMalloc.
+ * Same arguments, tables and errors as moe_mm_data, minus the workspace. The
+ * per-chunk expert counts go to a device array inside the library,
+ * Q8_MOE_NOALLOC_SCRATCH_BYTES (4 MiB) per GPU, reserved when the library is
+ * loaded on that GPU and held until the process ends; its address is looked
+ * up once per device on the first call (with the stream's device current).
+ * The call never allocates or frees. Requests whose counts do not fit
+ * (moe_mm_data_workspace_size(T, topk, E) above the limit, e.g. E = 1024 with
+ * T * topk above 262144) return Q8_EUNSUPPORTED before any HIP call. Every
+ * call on one GPU uses that GPU's one array: calls that overlap in time on one
+ * device (several streams or threads) race and must be serialised by the
+ * caller; calls in sequence on a stream are fine (each rewrites every count it
+ * reads).
+ */
+#define Q8_MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
+int moe_mm_data_noalloc(const int32_t* topk_ids, int64_t T, int topk, int E, int64_t n, int64_t k,
+                        int32_t* expert_offsets, int32_t* problem_sizes1, int32_t* problem_sizes2,
+                        int32_t* input_permutation, int32_t* output_permutation,
+                        hipStream_t stream);
+
+/*
  * Expert-grouped block-scaled FP8 GEMM.
  * "Implementation: Sgl project Sglang CUTLASS MoE" (cutlass_w4a8_moe_mm:
  * grouped GEMM over expert segments given by expert_offsets and

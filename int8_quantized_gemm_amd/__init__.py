@@ -44,7 +44,7 @@ EXPORTS = (
     "scaled_mm_int8",
     "scaled_mm_fp8",
     "moe_finalize",
-    "moe_mm_data_workspace_size", "moe_mm_data",
+    "moe_mm_data_workspace_size", "moe_mm_data", "moe_mm_data_noalloc",
     "grouped_blockwise_scaled_mm_workspace_size", "grouped_blockwise_scaled_mm",
     "shuffle_rows",
 )
@@ -72,6 +72,7 @@ _fin = _sig("moe_finalize", _i, _p, _i, _p, _p, _i64, _i, _i64, _p, _p)
 _fmm = _sig("scaled_mm_fp8", _i, _p, _p, _i64, _p, _p, _i64, _p, _p, _i, _i64, _i64, _i64, _p)
 _moe_ws = _sig("moe_mm_data_workspace_size", _sz, _i64, _i, _i)
 _moe = _sig("moe_mm_data", _i, _p, _i64, _i, _i, _i64, _i64, _p, _p, _p, _p, _p, _p, _sz, _p)
+_moe_na = _sig("moe_mm_data_noalloc", _i, _p, _i64, _i, _i, _i64, _i64, _p, _p, _p, _p, _p, _p)
 _gmm_ws = _sig("grouped_blockwise_scaled_mm_workspace_size", _sz, _i, _i64, _i64, _i64, _i, _i)
 _gmm = _sig("grouped_blockwise_scaled_mm", _i, _p, _p, _p, _p, _p, _i, _p, _p, _p, _p, _i, _i64,
             _i64, _i64, _i, _i, _p, _sz, _p)
@@ -396,6 +397,32 @@ def moe_mm_data(topk_ids: torch.Tensor, expert_offsets: torch.Tensor,
     _check(_moe(_ptr(topk_ids), T, topk, num_experts, n, k, _ptr(expert_offsets),
                 _ptr(problem_sizes1), _ptr(problem_sizes2), _ptr(input_permutation),
                 _ptr(output_permutation), ws, wsb, _stream(dev)))
+
+
+def moe_mm_data_noalloc(topk_ids: torch.Tensor, expert_offsets: torch.Tensor,
+                        problem_sizes1: torch.Tensor, problem_sizes2: torch.Tensor,
+                        input_permutation: torch.Tensor, output_permutation: torch.Tensor,
+                        num_experts: int, n: int, k: int) -> None:
+    """``moe_mm_data`` without a workspace (nothing is allocated: the counts go
+    to the library's own per-device scratch array, 4 MiB). For callers that
+    cannot allocate, such as code under graph capture; calls overlapping on one
+    device race."""
+    _contig(topk_ids, expert_offsets, problem_sizes1, problem_sizes2, input_permutation,
+            output_permutation)
+    for t in (topk_ids, expert_offsets, problem_sizes1, problem_sizes2, input_permutation,
+              output_permutation):
+        if t.dtype != torch.int32:
+            raise TypeError("routing tensors are int32")
+    T, topk = topk_ids.shape
+    if expert_offsets.numel() < num_experts + 1 or problem_sizes1.numel() < 3 * num_experts \
+            or problem_sizes2.numel() < 3 * num_experts \
+            or input_permutation.numel() < T * topk or output_permutation.numel() < T * topk:
+        raise ValueError("an output tensor is too small")
+    dev = _dev(topk_ids, expert_offsets, problem_sizes1, problem_sizes2, input_permutation,
+               output_permutation)
+    _check(_moe_na(_ptr(topk_ids), T, topk, num_experts, n, k, _ptr(expert_offsets),
+                   _ptr(problem_sizes1), _ptr(problem_sizes2), _ptr(input_permutation),
+                   _ptr(output_permutation), _stream(dev)))
 
 
 def moe_finalize(d: torch.Tensor, topk_weights: torch.Tensor | None, topk: int,

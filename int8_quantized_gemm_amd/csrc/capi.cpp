@@ -214,11 +214,14 @@ size_t moe_mm_data_workspace_size(int64_t T, int topk, int E) {
   return q8::moe_workspace_ints(T, topk, E) * sizeof(int32_t);
 }
 
-int moe_mm_data(const int32_t* topk_ids, int64_t T, int topk, int E, int64_t n, int64_t k,
-                int32_t* expert_offsets, int32_t* problem_sizes1, int32_t* problem_sizes2,
-                int32_t* input_permutation, int32_t* output_permutation, void* workspace,
-                size_t workspace_bytes, hipStream_t stream) {
-  static const char* fn = "moe_mm_data";
+}  // extern "C"
+
+namespace {
+// Shared argument rules of moe_mm_data and moe_mm_data_noalloc.
+int check_moe_args(const char* fn, const int32_t* topk_ids, int64_t T, int topk, int E, int64_t n,
+                   int64_t k, const int32_t* expert_offsets, const int32_t* problem_sizes1,
+                   const int32_t* problem_sizes2, const int32_t* input_permutation,
+                   const int32_t* output_permutation) {
   if (T < 0 || topk < 1) return fail(Q8_ESHAPE, "%s: need T >= 0 and topk >= 1", fn);
   if (E < 1 || E > 1024) return fail(Q8_EUNSUPPORTED, "%s: E must be in [1, 1024]", fn);
   if (T * (int64_t)topk >= kMaxI32) return fail(Q8_ESHAPE, "%s: T * topk must be below 2^31", fn);
@@ -227,6 +230,20 @@ int moe_mm_data(const int32_t* topk_ids, int64_t T, int topk, int E, int64_t n, 
     return fail(Q8_EINVAL, "%s: null pointer", fn);
   if (T > 0 && (!topk_ids || !input_permutation || !output_permutation))
     return fail(Q8_EINVAL, "%s: null pointer", fn);
+  return Q8_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_mm_data(const int32_t* topk_ids, int64_t T, int topk, int E, int64_t n, int64_t k,
+                int32_t* expert_offsets, int32_t* problem_sizes1, int32_t* problem_sizes2,
+                int32_t* input_permutation, int32_t* output_permutation, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  static const char* fn = "moe_mm_data";
+  const int r = check_moe_args(fn, topk_ids, T, topk, E, n, k, expert_offsets, problem_sizes1,
+                               problem_sizes2, input_permutation, output_permutation);
+  if (r != Q8_OK) return r;
   const size_t need = moe_mm_data_workspace_size(T, topk, E);
   if (need && (!workspace || workspace_bytes < need))
     return fail(Q8_EWORKSPACE, "%s: workspace needs %zu bytes", fn, need);
@@ -234,6 +251,28 @@ int moe_mm_data(const int32_t* topk_ids, int64_t T, int topk, int E, int64_t n, 
                                            problem_sizes1, problem_sizes2, input_permutation,
                                            output_permutation, static_cast<int32_t*>(workspace),
                                            stream),
+                    fn);
+}
+
+int moe_mm_data_noalloc(const int32_t* topk_ids, int64_t T, int topk, int E, int64_t n,
+                        int64_t k, int32_t* expert_offsets, int32_t* problem_sizes1,
+                        int32_t* problem_sizes2, int32_t* input_permutation,
+                        int32_t* output_permutation, hipStream_t stream) {
+  static const char* fn = "moe_mm_data_noalloc";
+  const int r = check_moe_args(fn, topk_ids, T, topk, E, n, k, expert_offsets, problem_sizes1,
+                               problem_sizes2, input_permutation, output_permutation);
+  if (r != Q8_OK) return r;
+  const size_t need = moe_mm_data_workspace_size(T, topk, E);
+  if (need > (size_t)Q8_MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(Q8_EUNSUPPORTED,
+                "%s: these routing tables need %zu bytes of scratch, above the %u bytes the "
+                "allocation-free entry point holds per device (call moe_mm_data with a workspace)",
+                fn, need, (unsigned)Q8_MOE_NOALLOC_SCRATCH_BYTES);
+  static_assert((size_t)Q8_MOE_NOALLOC_SCRATCH_BYTES == q8::kNoAllocInts * sizeof(int32_t),
+                "header limit and device array agree");
+  return hip_status(q8::launch_moe_mm_data_noalloc(topk_ids, T, topk, E, n, k, expert_offsets,
+                                                   problem_sizes1, problem_sizes2,
+                                                   input_permutation, output_permutation, stream),
                     fn);
 }
 

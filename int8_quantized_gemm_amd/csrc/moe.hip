@@ -20,6 +20,9 @@
 //                   the chunk (counted from an LDS copy of the chunk), so
 //                   slots ascend with the flat index inside every expert and
 //                   the tables are deterministic.
+#include <atomic>
+#include <mutex>
+
 #include "q8_internal.h"
 #include "q8_device.h"
 
@@ -211,6 +214,56 @@ hipError_t launch_moe_mm_data(const int32_t* ids, int64_t T, int topk, int E, in
                        E, ws, in_perm, out_perm);
   }
   return hipGetLastError();
+}
+
+// ---- allocation-free routing ----------------------------------------------------
+// moe_mm_data_noalloc keeps its per-chunk expert counts (the only memory the
+// three routing kernels use besides their inputs and outputs) in this
+// file-scope array instead of a caller workspace: kNoAllocInts ints per device,
+// held until the process ends. In host code `scratch` is only a host-side
+// stand-in for the symbol; its device address on each GPU comes from
+// hipGetSymbolAddress, looked up once per device with that device current and
+// kept in scratch_on[]. moe_count overwrites every count a call reads, so
+// nothing has to start at zero; two calls that overlap on one device share the
+// array and race.
+static __device__ __align__(256) int32_t scratch[kNoAllocInts];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t*> scratch_on[kMaxDevices];
+std::mutex scratch_mu;
+}  // namespace
+
+hipError_t noalloc_scratch(int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int32_t* p = scratch_on[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    p = scratch_on[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!addr) return hipErrorInvalidSymbol;
+      p = static_cast<int32_t*>(addr);
+      scratch_on[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_moe_mm_data_noalloc(const int32_t* ids, int64_t T, int topk, int E, int64_t nk,
+                                      int64_t kk, int32_t* offsets, int32_t* ps1, int32_t* ps2,
+                                      int32_t* in_perm, int32_t* out_perm, hipStream_t st) {
+  if (moe_workspace_ints(T, topk, E) > (size_t)kNoAllocInts) return hipErrorInvalidValue;
+  int32_t* ws = nullptr;
+  const hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return launch_moe_mm_data(ids, T, topk, E, nk, kk, offsets, ps1, ps2, in_perm, out_perm, ws, st);
 }
 
 hipError_t launch_shuffle_rows(const void* src, int64_t row_bytes, const int32_t* map,

@@ -64,6 +64,13 @@ hipError_t launch_moe_mm_data(const int32_t* topk_ids, int64_t T, int topk, int 
                               int64_t n, int64_t k, int32_t* offsets, int32_t* ps1,
                               int32_t* ps2, int32_t* in_perm, int32_t* out_perm,
                               int32_t* ws, hipStream_t stream);
+// allocation-free variant: the counts live in a file-scope device array of
+// kNoAllocInts ints per device (the front end rejects larger requests)
+constexpr int64_t kNoAllocInts = 1 << 20;
+hipError_t launch_moe_mm_data_noalloc(const int32_t* topk_ids, int64_t T, int topk, int E,
+                                      int64_t n, int64_t k, int32_t* offsets, int32_t* ps1,
+                                      int32_t* ps2, int32_t* in_perm, int32_t* out_perm,
+                                      hipStream_t stream);
 hipError_t launch_moe_finalize(const void* D, bool bf16, const float* w, const int32_t* perm,
                                int64_t T, int topk, int64_t N, void* out, hipStream_t stream);
 hipError_t launch_shuffle_rows(const void* src, int64_t row_bytes, const int32_t* dst2src,

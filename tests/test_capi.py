@@ -177,3 +177,15 @@ def test_quant_scale_ue8m0_range(q8):
     assert q8._quant(8, q8.Q8_BF16, 4, 128, 128, 8, q8.Q8_E4M3FN, 8, 32, 0, 1e-10, -448, 448, 3, 0, p, 0, p, 0, p) == q8.Q8_EINVAL
     assert "scale_ue8m0" in q8.last_error()
     assert q8._quant(p, q8.Q8_BF16, 0, 128, 128, p, q8.Q8_E4M3FN, p, 32, 0, 1e-10, -448, 448, 2, 0, p, 0, p, 0, p) == q8.Q8_OK
+
+
+def test_noalloc_routing_rejects_beyond_its_scratch_on_the_host(q8):
+    """moe_mm_data_noalloc holds 4 MiB of counts per device: larger routings
+    are refused before any HIP call (so this runs without a GPU)."""
+    T, topk, E = 40000, 8, 1024
+    assert q8._moe_ws(T, topk, E) > (4 << 20)
+    st = q8._moe_na(8, T, topk, E, 16, 16, 8, 8, 8, 8, 8, None)
+    assert st == q8.Q8_EUNSUPPORTED and "scratch" in q8.last_error()
+    # the shared argument rules apply as for moe_mm_data
+    assert q8._moe_na(8, 4, 2, 0, 16, 16, 8, 8, 8, 8, 8, None) == q8.Q8_EUNSUPPORTED
+    assert q8._moe_na(8, 4, 2, 8, 16, 16, None, 8, 8, 8, 8, None) == q8.Q8_EINVAL
