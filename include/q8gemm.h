@@ -137,8 +137,11 @@ int quant_8bit(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, int64_t ld
  * A, W and As each below 4 GiB (Q8_EUNSUPPORTED otherwise).
  * Accumulation: FP8 products summed in float32 per K block, scaled and
  * summed in float32.
- * workspace: blockwise_scaled_mm_workspace_size() bytes (0 today; reserved
- * for split-K partials).
+ * workspace: blockwise_scaled_mm_workspace_size() bytes, 16-byte aligned:
+ * float32 split-K partials for decode batches of 17..64 rows (S x M x N
+ * floats, S the number of K ranges; 4 MiB for 64 x 4096 x 7168), 0 for every
+ * other shape (then NULL is allowed). Q8_EWORKSPACE if it is needed and
+ * missing or short. The contents need no initialisation and are overwritten.
  */
 size_t blockwise_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K, int bn, int bk);
 int blockwise_scaled_mm(const void* A, const float* As, const void* W, const float* Ws,

@@ -115,25 +115,33 @@ int quant_8bit(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, int64_t ld
   return hip_status(q8::launch_quant(a, stream), fn);
 }
 
-size_t blockwise_scaled_mm_workspace_size(int64_t, int64_t, int64_t, int, int) { return 0; }
+size_t blockwise_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K, int bn, int bk) {
+  if (M < 0 || N < 1 || K < 1 || (bk != 32 && bk != 128) || bn < 16 || bn % 16 != 0 || K % bk != 0)
+    return 0;
+  return q8::blockwise_workspace_bytes(M, N, K, bn, bk);
+}
 
 int blockwise_scaled_mm(const void* A, const float* As, const void* W, const float* Ws,
                         const void* bias, void* D, q8_dtype out_dtype, int64_t M, int64_t N,
                         int64_t K, int bn, int bk, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {
   static const char* fn = "blockwise_scaled_mm";
-  (void)workspace;
-  (void)workspace_bytes;
   if (!is_16bit_out(out_dtype)) return fail(Q8_EINVAL, "%s: out_dtype must be BF16 or F16", fn);
   int r = check_block_shape(fn, M, N, K, bn, bk);
   if (r != Q8_OK) return r;
   if (M == 0) return ok();
   if (!A || !As || !W || !Ws || !D) return fail(Q8_EINVAL, "%s: null pointer", fn);
+  const size_t need = blockwise_scaled_mm_workspace_size(M, N, K, bn, bk);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(Q8_EWORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  if (need && (uintptr_t)workspace % 16 != 0)
+    return fail(Q8_EINVAL, "%s: workspace must be 16-byte aligned", fn);
   q8::BlockGemmArgs a{};
   a.A = static_cast<const uint8_t*>(A); a.As = As;
   a.W = static_cast<const uint8_t*>(W); a.Ws = Ws;
   a.bias = bias; a.D = D; a.out_dtype = out_dtype;
   a.M = M; a.N = N; a.K = K; a.bn = bn; a.bk = bk;
+  a.workspace = need ? workspace : nullptr;
   return hip_status(q8::launch_blockwise(a, stream), fn);
 }
 

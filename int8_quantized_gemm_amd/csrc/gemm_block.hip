@@ -72,6 +72,23 @@ __device__ __forceinline__ f32x4 mfma_fp8_k128(const i32x8& a, const i32x8& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
 }
 
+// One 32-wide K block of a 16x16x128 MFMA on its own. The MX-scaled form
+// takes one E8M0 scale byte per lane and operand, lane r + 16 kb supplying
+// block kb's scale of row r, in the instruction's K order (lane group g
+// holds K [16g, 16g+16) in its first four registers and [64+16g, 64+16g+16)
+// in its last four; block kb is K [32kb, 32kb+32)). With byte 127 (2^0) in
+// lane group s and byte 0 (2^-127) elsewhere, on both operands, block s is
+// multiplied by exactly 1 and every other block by 2^-254, which puts each of
+// their products (at most 448^2 * 32 < 2^23 per block) below half the
+// smallest float32 subnormal: they contribute exactly zero, and the result
+// is block s's partial product with no VALU masking of the operands.
+__device__ __forceinline__ int block_selector(int g, int s) { return g == s ? 127 : 0; }
+
+__device__ __forceinline__ f32x4 mfma_block(const i32x8& w, const i32x8& a, int sel) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, a, z, 0, 0, 0, sel, 0, sel);
+}
+
 __device__ __forceinline__ f32x4 mfma_fp8_k32(long a, long b) {
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, z, 0, 0, 0);
@@ -746,6 +763,16 @@ __device__ __forceinline__ i32x8 gload32(const uint8_t* p) {
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Fragment layout of gemm_stream_sel and gemm_stream_sa: lane group g holds bytes [16g, 16g+16)
+// (first half) and [64+16g, 64+16g+16) (second half) of each 128-byte chunk,
+// so each load instruction reads a contiguous 64-byte half of sixteen weight
+// rows (measured: M = 16 10.9 -> 10.5 us against 32-byte lane pieces).
+__device__ __forceinline__ i32x8 gload_halves(const uint8_t* p) {
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 64);
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 // One workgroup per 16 weight rows (x one 16*MT-row activation block); its
 // NW waves split the 128-byte K chunks and issue every load of their share
 // before any math, so the whole weight slice is in flight at once. Lane group
@@ -837,17 +864,110 @@ __global__ __launch_bounds__(NW * 64) void gemm_stream(TileParams p) {
 }
 
 // ------------------------------------------------------------------------------
+// Streaming (decode) kernel for 32-wide K blocks and few activation rows
+// ------------------------------------------------------------------------------
+// One 16x16x128 MFMA over a 128-byte chunk yields every 32-wide block partial
+// of four activation rows at once: column j of the activation operand carries
+// row m = 4t + j/4 restricted to K block b = j%4 of the chunk (zero outside
+// it), so D[n, j] = P_b[n, m]. Lane group g holds bytes [32g, 32g+32) of the
+// chunk for both operands — block g — so column j's lane in group g loads its
+// 32 activation bytes only when g == j%4 and is zero otherwise. MT4 MFMAs per
+// chunk cover 4*MT4 activation rows (against one MFMA per block and 16-row
+// block for a dense activation operand). A lane's four outputs share (m, b):
+// one scale product As[m, kb] * Ws[n/bn, kb] per MFMA. After the K loop the
+// four block residues b of a row are summed across the adjacent lanes (a fixed
+// pairing, so every lane holds the same bits), then over the waves in a fixed
+// order.
+template <int MT4, int NW, int R>
+__global__ __launch_bounds__(NW * 64) void gemm_stream_pk(TileParams p) {
+  __shared__ f32x4 red[NW][MT4][16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int b = r16 & 3, q = r16 >> 2;
+  const int64_t N = p.N, K = p.K, M = p.M;
+  const int KB = p.KB;  // K / 32
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int NC = (int)(K / 128);
+  const int c_b = (int)((int64_t)w * NC / NW), c_e = (int)((int64_t)(w + 1) * NC / NW);
+
+  const int64_t nrow = n0 + r16 < N ? n0 + r16 : N - 1;
+  const uint8_t* wp = p.W + nrow * K + 32 * g;
+  const float* wsp = p.Ws + (n0 / p.bn) * KB + b;  // n0, bn multiples of 16: one block
+  const uint8_t* ap[MT4];
+  const float* asp[MT4];
+  bool act[MT4], has[MT4];
+#pragma unroll
+  for (int t = 0; t < MT4; ++t) {
+    const int64_t m = 4 * t + q;
+    has[t] = m < M;
+    act[t] = has[t] && g == b;
+    const int64_t mc = has[t] ? m : M - 1;
+    ap[t] = p.A + mc * K + 32 * g;
+    asp[t] = p.As + mc * KB + b;
+  }
+
+  f32x4 acc[MT4];
+#pragma unroll
+  for (int t = 0; t < MT4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const i32x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+
+  for (int c0 = c_b; c0 < c_e; c0 += R) {
+    i32x8 wf[R], af[R][MT4];
+    float sa[R][MT4], ws[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int c = c0 + u < c_e ? c0 + u : c_e - 1;
+      wf[u] = gload32(wp + (int64_t)c * 128);
+#pragma unroll
+      for (int t = 0; t < MT4; ++t) af[u][t] = act[t] ? gload32(ap[t] + (int64_t)c * 128) : zero8;
+      ws[u] = wsp[4 * c];
+#pragma unroll
+      for (int t = 0; t < MT4; ++t) sa[u][t] = has[t] ? asp[t][4 * c] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      if (c0 + u >= c_e) break;
+#pragma unroll
+      for (int t = 0; t < MT4; ++t) {
+        const f32x4 pr = mfma_fp8_k128(wf[u], af[u][t]);
+        acc[t] = fma4s(pr, sa[u][t] * ws[u], acc[t]);
+      }
+    }
+  }
+
+  // sum the four block residues of each activation row: (b0 + b1) + (b2 + b3)
+#pragma unroll
+  for (int t = 0; t < MT4; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = acc[t][i];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      acc[t][i] = v;
+    }
+    if (b == 0) red[w][t][4 * g + q] = acc[t];
+  }
+  __syncthreads();
+  // fixed-order sum over the waves; entry e = 4g + q holds W rows n0 + 4g ..
+  // n0 + 4g + 3 of activation row 4t + q
+  const bool bf16 = p.out_bf16 != 0;
+  const bool vec = p.d_vec4 != 0;
+  for (int idx = tid; idx < MT4 * 16; idx += NW * 64) {
+    const int t = idx >> 4, e = idx & 15;
+    const int64_t m = 4 * t + (e & 3);
+    if (m >= M) continue;
+    f32x4 sum = red[0][t][e];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) sum += red[ww][t][e];
+    const int64_t n = n0 + 4 * (e >> 2);
+    if (n < N) store4(p, m, n, p.bias ? sum + load_bias4(p.bias, n, N, bf16, vec && n + 3 < N) : sum, bf16, vec);
+  }
+}
+
+// ------------------------------------------------------------------------------
 // Streaming (decode) kernel with shared activations: M <= 16, K a multiple of 1024
 // ------------------------------------------------------------------------------
-// Fragment layout of gemm_stream_sa: lane group g holds bytes [16g, 16g+16)
-// (first half) and [64+16g, 64+16g+16) (second half) of each 128-byte chunk,
-// so each load instruction reads a contiguous 64-byte half of sixteen weight
-// rows (measured: M = 16 10.9 -> 10.5 us against 32-byte lane pieces).
-__device__ __forceinline__ i32x8 gload_halves(const uint8_t* p) {
-  const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
-  const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 64);
-  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
 
 // The part of such a fragment that belongs to 32-wide K block s of the chunk:
 // the half s>>1 of the lane groups with g>>1 == s&1; everything else zeroed.
@@ -971,6 +1091,185 @@ void gemm_stream_sa(TileParams p) {
 }
 
 // ------------------------------------------------------------------------------
+// Split-K streaming kernel for decode batches of 17..64 activation rows
+// ------------------------------------------------------------------------------
+// A workgroup that owns 16 weight rows for all of K needs the whole activation
+// (M x K bytes) from L2: at 64 rows that is four times the weight bytes it
+// streams, and those L2 reads, not the HBM stream, set the time. Here a
+// workgroup owns 64 weight rows (four 16-row blocks) and one of S K ranges of
+// Kc = K/S bytes: it copies the activation slice [M, Kc] and its scales into
+// LDS once (buffer->LDS, so the copies are in flight with the weight loads),
+// streams its 64 x Kc weight bytes (each wave issues all of its loads up
+// front), and writes its float32 partial [M, 64] for that K range;
+// gemm_split_reduce then sums the S partials of every output in a fixed
+// order (deterministic), adds the bias and rounds.
+// MFMA columns: for 128-wide K blocks, sixteen activation rows (one MFMA per
+// chunk and 16-row block); for 32-wide blocks, (row, block) pairs packed as
+// in gemm_stream_pk (four rows x four blocks per MFMA), so each MFMA's
+// partials are already per block and one scale product serves a lane.
+// LDS activation slice: dense [M, Kc], 16-byte piece j of row m stored at
+// piece position j ^ (m & 15) (Kc a multiple of 256 bytes keeps every row's
+// pieces inside the row); sixteen lanes reading one piece of sixteen rows
+// then hit sixteen different bank groups. The XOR is applied through the
+// source address of the copies, whose LDS side is contiguous.
+constexpr int kMidRows = 64;   // weight rows per workgroup
+constexpr int kMidNW = 8;      // waves: 4 row blocks x 2 chunk parities
+
+template <int KS, int MT, int R>
+__global__ __launch_bounds__(kMidNW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void gemm_split_mid(TileParams p, float* __restrict__ part, int Kc) {
+  constexpr int KSUB = 128 / KS;
+  constexpr int NP = kMidNW / 4;  // chunk parities (waves per row block)
+  static_assert(R * KSUB <= 64, "a wave's weight scales fit one register");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rb = w & 3, h = w >> 2;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t N = p.N, K = p.K, M = p.M;
+  const int KB = p.KB;
+  const int s_idx = blockIdx.y;
+  const int64_t k0 = (int64_t)s_idx * Kc;
+  const int kb0 = (int)(k0 / KS);
+  const int kbc = Kc / KS;          // K blocks in the slice
+  const int ncc = Kc / 128;         // chunks in the slice
+  const int pr = Kc / 16;           // 16-byte pieces per activation row
+  const int64_t n0 = (int64_t)blockIdx.x * kMidRows;
+  uint8_t* sA = smem;
+  const uint32_t a_bytes = (uint32_t)(((M * Kc) + 1023) & ~1023LL);
+  float* sS = reinterpret_cast<float*>(smem + a_bytes);
+
+  // ---- activation slice and its scales -> LDS
+  {
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (uint32_t)(M * K));
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(p.As, (uint32_t)(M * KB * 4));
+    const int pieces = (int)M * pr;
+    for (int i = w; i * 64 < pieces; i += kMidNW) {
+      const int pc = i * 64 + lane;
+      const int row = pc / pr, j = pc - row * pr;
+      // slot (row, j) holds piece j ^ key(row); lanes past the slice read
+      // zeros (offset beyond the resource) into the padding
+      const uint32_t src = pc < pieces ? (uint32_t)(row * K + k0 + 16 * (j ^ (row & 15))) : 0xFFFFFFF0u;
+      b2l16(rA, src, 0, sA + i * 1024);
+    }
+    const int nsc = (int)M * kbc;
+    for (int i = w; i * 64 < nsc; i += kMidNW) {
+      const int f = i * 64 + lane;
+      const int row = f / kbc, c = f - row * kbc;
+      const uint32_t src = f < nsc ? (uint32_t)((row * KB + kb0 + c) * 4) : 0xFFFFFFF0u;
+      b2l4(rS, src, 0, sS + i * 64);
+    }
+  }
+  // ---- this wave's weight chunks (row block rb, chunks h, h + NP, ...), all
+  // issued before any wait; lane group g holds bytes [16g, 16g+16) and
+  // [64+16g, 64+16g+16) of each chunk (the MX-scaled MFMA's K order, in which
+  // 32-wide block s of the chunk is the instruction's block s)
+  const int64_t nrow = n0 + 16 * rb + r16 < N ? n0 + 16 * rb + r16 : N - 1;
+  const uint8_t* wp = p.W + nrow * K + k0 + 16 * g;
+  int64_t nb = (n0 + 16 * rb) / p.bn;
+  if (nb > p.nbw - 1) nb = p.nbw - 1;
+  // this row block's weight scales of the slice, one per lane (wave-uniform
+  // per block): lane i holds block kb0 + (chunk h + (i / KSUB) * NP) * KSUB + i % KSUB
+  const int li = lane < R * KSUB ? lane : R * KSUB - 1;
+  const int lc = h + (li / KSUB) * NP;
+  const float wsl = p.Ws[nb * KB + kb0 + (lc < ncc ? lc : ncc - 1) * KSUB + li % KSUB];
+  asm volatile("" ::: "memory");
+  i32x8 wf[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int cc0 = h + u * NP;
+    const int cc = cc0 < ncc ? cc0 : ncc - 1;
+    wf[u] = gload_halves(wp + (int64_t)cc * 128);
+  }
+  // the copies were issued first and loads complete in order: once at most
+  // 2R (weight halves) + 1 (scales) remain, this wave's copies have landed;
+  // the barrier without a fence keeps the weight loads in flight across it
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * R + 1) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // LDS byte offsets of this lane's fragment pieces and scales for its
+  // first chunk (h), per 16-row block t. Chunk h + NP u (NP = 2) adds 256 u
+  // bytes to every piece offset: piece (8 cc + x) ^ key with x = 8h + 4f + g
+  // < 16 and key < 16 is 16 u + (x ^ key). Rows past M repeat the last row
+  // (never stored).
+  static_assert(NP == 2, "piece offsets assume two chunk parities");
+  uint32_t aoff[MT][2], soff[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = 16 * t + r16 < M ? 16 * t + r16 : (int)M - 1;
+    const int key = m & 15;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) aoff[t][f] = (uint32_t)(m * Kc + 16 * ((8 * h + 4 * f + g) ^ key));
+    soff[t] = (uint32_t)((m * kbc + h * KSUB) * 4);
+  }
+  const uint8_t* sSb = reinterpret_cast<const uint8_t*>(sS);
+  // fragments of (u, t) read one step ahead of their MFMAs
+  i32x8 afb[2];
+  f32x4 sab[2];
+  auto load = [&](int u, int t, int b) {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(sA + aoff[t][0] + 256 * u);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(sA + aoff[t][1] + 256 * u);
+    afb[b] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    if constexpr (KSUB == 4) sab[b] = *reinterpret_cast<const f32x4*>(sSb + soff[t] + 32 * u);
+    else sab[b][0] = *reinterpret_cast<const float*>(sSb + soff[t] + 8 * u);
+  };
+  f32x4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (h < ncc) load(0, 0, 0);
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int cc = h + u * NP;
+    if (cc >= ncc) break;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int b = (u * MT + t) & 1;
+      if (t + 1 < MT) load(u, t + 1, b ^ 1);
+      else if (u + 1 < R && cc + NP < ncc) load(u + 1, 0, b ^ 1);
+#pragma unroll
+      for (int s = 0; s < KSUB; ++s) {
+        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsl), u * KSUB + s));
+        const f32x4 pr = KS == 32 ? mfma_block(wf[u], afb[b], block_selector(g, s)) : mfma_fp8_k128(wf[u], afb[b]);
+        acc[t] = fma4s(pr, sab[b][s] * ws, acc[t]);
+      }
+    }
+  }
+  // the NP waves of a row block -> one partial, summed in parity order
+  __syncthreads();  // every wave is done with the activation slice
+  f32x4* red = reinterpret_cast<f32x4*>(smem);  // [kMidNW][MT][64]
+#pragma unroll
+  for (int t = 0; t < MT; ++t) red[(w * MT + t) * 64 + lane] = acc[t];
+  __syncthreads();
+  if (h == 0) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      f32x4 v = red[(rb * MT + t) * 64 + lane];
+#pragma unroll
+      for (int hh = 1; hh < NP; ++hh) v += red[((rb + 4 * hh) * MT + t) * 64 + lane];
+      const int64_t m = 16 * t + r16;
+      const int64_t n = n0 + 16 * rb + 4 * g;
+      if (m < M && n < N) *reinterpret_cast<f32x4*>(part + ((int64_t)s_idx * M + m) * N + n) = v;
+    }
+  }
+}
+
+// D[m, n .. n+3] = sum_s part[s][m][n .. n+3] (s ascending) + bias, rounded.
+__global__ __launch_bounds__(256) void gemm_split_reduce(TileParams p, const float* __restrict__ part,
+                                                         int S) {
+  const int64_t N = p.N, M = p.M;
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nv = N / 4;
+  if (v >= M * nv) return;
+  const int64_t m = v / nv, n = (v - m * nv) * 4;
+  f32x4 sum = *reinterpret_cast<const f32x4*>(part + m * N + n);
+  for (int s = 1; s < S; ++s) sum += *reinterpret_cast<const f32x4*>(part + ((int64_t)s * M + m) * N + n);
+  const bool bf16 = p.out_bf16 != 0;
+  const bool vec = p.d_vec4 != 0;
+  store4(p, m, n, p.bias ? sum + load_bias4(p.bias, n, N, bf16, vec) : sum, bf16, vec);
+}
+
+// ------------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------------
 constexpr int kSkinnyMaxM = 64;
@@ -1051,6 +1350,22 @@ hipError_t launch_stream_sa(const TileParams& tp, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int MT4>
+hipError_t launch_stream_pk_mt(const TileParams& tp, hipStream_t st) {
+  // eight waves of seven chunks each (K = 7168: every load of the workgroup
+  // in flight at once; measured M = 1 8.3 -> 8.0 us and M = 4 9.0 -> 8.3 us
+  // against sixteen waves of four)
+  constexpr int NW = 8, R = 7;
+  if ((tp.N + 15) / 16 > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((gemm_stream_pk<MT4, NW, R>), dim3((unsigned)((tp.N + 15) / 16)), dim3(NW * 64), 0, st, tp);
+  return hipGetLastError();
+}
+
+// 32-wide K blocks, M <= 8: MFMAs packing four activation rows each
+hipError_t launch_stream_pk(const TileParams& tp, hipStream_t st) {
+  return tp.M <= 4 ? launch_stream_pk_mt<1>(tp, st) : launch_stream_pk_mt<2>(tp, st);
+}
+
 template <int KS>
 hipError_t launch_stream(const TileParams& tp, hipStream_t st) {
   const int64_t mt = (tp.M + 15) / 16;
@@ -1060,6 +1375,78 @@ hipError_t launch_stream(const TileParams& tp, hipStream_t st) {
     case 3: return launch_stream_mt<KS, 3>(tp, st);
     default: return launch_stream_mt<KS, 4>(tp, st);
   }
+}
+
+// ---- split-K decode for 17..64 rows ----------------------------------------------
+struct MidPlan {
+  int S = 0;      // K ranges (grid.y)
+  int Kc = 0;     // bytes of K per range
+  int mt = 0;     // 16-row activation blocks
+  int R = 0;      // chunks per wave (loads issued up front)
+  int64_t lds = 0;
+};
+
+// K ranges: the fewest that give 256 workgroups, each range a multiple of 256
+// bytes and at most 2048 (so a wave's chunks fit its registers); none fits ->
+// not this kernel.
+inline bool mid_plan(int64_t M, int64_t N, int64_t K, int bk, MidPlan& pl) {
+  if (M < 17 || M > kSkinnyMaxM || N % 4 != 0) return false;
+  const int64_t groups = (N + kMidRows - 1) / kMidRows;
+  int best = 0;
+  for (int S = 1; S <= 32; S *= 2) {
+    if (K % (256LL * S) != 0) continue;
+    if (K / S > 2048) continue;
+    best = S;
+    if (groups * S >= 256) break;
+  }
+  if (!best || groups * best > 0x7FFFFFFFLL) return false;
+  pl.S = best;
+  pl.Kc = (int)(K / best);
+  const int ncc = pl.Kc / 128;
+  const int need = (ncc + kMidNW / 4 - 1) / (kMidNW / 4);
+  pl.R = need <= 4 ? 4 : 8;
+  pl.mt = (int)((M + 15) / 16);
+  const int64_t kbc = pl.Kc / bk;
+  const int64_t a_bytes = ((M * pl.Kc) + 1023) & ~1023LL;
+  const int64_t s_bytes = ((M * kbc + 63) / 64) * 64 * 4;
+  const int64_t red_bytes = (int64_t)kMidNW * pl.mt * 64 * 16;
+  pl.lds = a_bytes + s_bytes > red_bytes ? a_bytes + s_bytes : red_bytes;
+  return pl.lds <= kLdsBytes;
+}
+
+template <int KS, int MT, int R>
+hipError_t launch_mid_inst(const TileParams& tp, const MidPlan& pl, float* part, hipStream_t st) {
+  const auto kern = gemm_split_mid<KS, MT, R>;
+  static std::atomic<uint64_t> lds_raised{0};
+  hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kern), lds_raised);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((tp.N + kMidRows - 1) / kMidRows), (unsigned)pl.S);
+  hipLaunchKernelGGL(kern, grid, dim3(kMidNW * 64), (unsigned)pl.lds, st, tp, part, pl.Kc);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t vecs = tp.M * (tp.N / 4);
+  hipLaunchKernelGGL(gemm_split_reduce, dim3((unsigned)((vecs + 255) / 256)), dim3(256), 0, st, tp,
+                     (const float*)part, pl.S);
+  return hipGetLastError();
+}
+
+template <int KS, int MT>
+hipError_t launch_mid_r(const TileParams& tp, const MidPlan& pl, float* part, hipStream_t st) {
+  return pl.R == 4 ? launch_mid_inst<KS, MT, 4>(tp, pl, part, st)
+                   : launch_mid_inst<KS, MT, 8>(tp, pl, part, st);
+}
+
+template <int KS>
+hipError_t launch_mid_ks(const TileParams& tp, const MidPlan& pl, float* part, hipStream_t st) {
+  switch (pl.mt) {
+    case 2: return launch_mid_r<KS, 2>(tp, pl, part, st);
+    case 3: return launch_mid_r<KS, 3>(tp, pl, part, st);
+    default: return launch_mid_r<KS, 4>(tp, pl, part, st);
+  }
+}
+
+hipError_t launch_mid(const TileParams& tp, const MidPlan& pl, int bk, float* part, hipStream_t st) {
+  return bk == 32 ? launch_mid_ks<32>(tp, pl, part, st) : launch_mid_ks<128>(tp, pl, part, st);
 }
 
 constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 4;
@@ -1116,6 +1503,14 @@ __global__ void invert_permutation(const int32_t* __restrict__ perm, int64_t n,
 
 }  // namespace
 
+size_t blockwise_workspace_bytes(int64_t M, int64_t N, int64_t K, int bn, int bk) {
+  (void)bn;
+  if (K % 128 != 0) return 0;
+  MidPlan pl;
+  if (!mid_plan(M, N, K, bk, pl)) return 0;
+  return (size_t)pl.S * (size_t)M * (size_t)N * sizeof(float);
+}
+
 hipError_t launch_blockwise(const BlockGemmArgs& a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   const TileParams tp = make_params(a);
@@ -1124,12 +1519,19 @@ hipError_t launch_blockwise(const BlockGemmArgs& a, hipStream_t st) {
   // the streaming kernel reads a chunk's four 32-wide activation scales as
   // one 16-byte vector
   if (a.M <= kSkinnyMaxM) {
+    // 17..64 rows: split-K over 64-row workgroups, partials in the workspace
+    MidPlan pl;
+    if (mid_plan(a.M, a.N, a.K, a.bk, pl) && a.workspace && (uintptr_t)a.workspace % 16 == 0 &&
+        (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.As % 16 == 0)
+      return launch_mid(tp, pl, a.bk, static_cast<float*>(a.workspace), st);
     // from 8 activation rows on, staging them once per workgroup beats every
     // wave reading them from L2 (measured: M = 16 12.2 -> 10.8 us, M = 1 and
     // 4 slightly slower staged)
     if (a.M >= 8 && stream_sa_fits(a.M, a.K, tp.KB) && (uintptr_t)a.A % 16 == 0 &&
         (uintptr_t)a.As % 16 == 0)
       return a.bk == 128 ? launch_stream_sa<128>(tp, st) : launch_stream_sa<32>(tp, st);
+    // up to 8 rows and 32-wide blocks: four rows' block partials per MFMA
+    if (a.bk == 32 && a.M <= 8) return launch_stream_pk(tp, st);
     return a.bk == 128 ? launch_stream<128>(tp, st) : launch_stream<32>(tp, st);
   }
   const int64_t tiles = tp.tiles_m * tp.tiles_n;

@@ -35,7 +35,10 @@ struct BlockGemmArgs {
   int E;
   int64_t w_expert_stride;        // bytes between experts in W
   int64_t ws_expert_stride;       // floats between experts in Ws
+  void* workspace;                // split-K partials (dense call), or null
 };
+// workspace bytes the dense call needs for this shape (0: none)
+size_t blockwise_workspace_bytes(int64_t M, int64_t N, int64_t K, int bn, int bk);
 hipError_t launch_blockwise(const BlockGemmArgs& a, hipStream_t stream);
 hipError_t launch_grouped(const BlockGemmArgs& a, int64_t total_m, int32_t* c_inv_ws,
                           const int32_t* c_map, hipStream_t stream);

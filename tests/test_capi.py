@@ -107,6 +107,19 @@ def test_blockwise_validation(q8):
     assert q8._bmm(*args(4, 256, 512, 128, 128)) == q8.Q8_EINVAL          # null pointers
     assert q8._bmm(*args(0, 256, 512, 128, 128)) == q8.Q8_OK              # M = 0
     assert q8._bmm(*args(-1, 256, 512, 128, 128)) == q8.Q8_ESHAPE
+    # 17..64 rows split K into ranges whose float32 partials need a workspace:
+    # 4 ranges of 1792 bytes for K = 7168 (256 workgroups of 64 weight rows)
+    assert q8._bmm_ws(33, 4096, 7168, 32, 32) == 4 * 33 * 4096 * 4
+    assert q8._bmm_ws(64, 4096, 7168, 128, 128) == 4 * 64 * 4096 * 4
+    assert q8._bmm_ws(17, 1000, 1024, 128, 128) == 4 * 17 * 1000 * 4
+    for M, N in ((16, 4096), (65, 4096), (33, 1002)):  # other kernels, or N % 4
+        assert q8._bmm_ws(M, N, 7168, 128, 128) == 0
+    wargs = lambda ws, wsb: (8, 8, 8, 8, p, 8, q8.Q8_BF16, 33, 4096, 7168, 32, 32, ws, wsb, p)
+    assert q8._bmm(*wargs(p, 0)) == q8.Q8_EWORKSPACE
+    assert "workspace" in q8.last_error()
+    assert q8._bmm(*wargs(16, 4 * 33 * 4096 * 4 - 1)) == q8.Q8_EWORKSPACE
+    assert q8._bmm(*wargs(20, 4 * 33 * 4096 * 4)) == q8.Q8_EINVAL     # misaligned
+    assert "aligned" in q8.last_error()
 
 
 def test_int8_validation(q8):

@@ -79,11 +79,14 @@ def test_decode_shared_activation_shapes(M, N, K, bk):
 
 @pytest.mark.parametrize("M,N,K,bn,bk", [(17, 1000, 1024, 128, 128), (33, 4096, 7168, 32, 32),
                                         (48, 520, 2048, 32, 32), (64, 300, 512, 128, 128),
-                                        (40, 4096, 7168, 128, 128), (30, 600, 1024, 48, 128)])
+                                        (40, 4096, 7168, 128, 128), (30, 600, 1024, 48, 128),
+                                        (64, 4096, 7168, 32, 32), (20, 1002, 1024, 128, 128),
+                                        (24, 16, 4096, 32, 32)])
 def test_decode_mid_rows(M, N, K, bn, bk):
-    """17 .. 64 activation rows (two to four 16-row activation blocks per
-    wave in the streaming kernel): ragged N, bias, fewer K chunks than waves,
-    bn != bk."""
+    """17 .. 64 activation rows: K split into ranges whose float32 partials
+    a second kernel sums (ragged N, bias, a range of two chunks (K = 1024 in
+    four), one 64-row workgroup column (N = 16), bn != bk), and N not a
+    multiple of 4, which takes the kernel without partials."""
     run_case(M, N, K, bn, bk, ue=(bk == 32), bias=True, seed=M + N)
 
 
