@@ -517,7 +517,7 @@ class _Null:
 
 def traffic_probe(torch, q8, synth) -> int:
     """Kernels for the HBM byte counters: three prefill GEMM launches, three
-    decode GEMM launches at M=1 and at M=16, and three MoE grouped GEMM
+    decode GEMM launches each at M=1, 16 and 64, and three MoE grouped GEMM
     launches (a 256 MiB fill before each, so the operands are not resident in
     the Infinity Cache), and three plain 256 MiB device-to-device copies of
     known size (the scale for FETCH_SIZE / WRITE_SIZE)."""
@@ -536,12 +536,13 @@ def traffic_probe(torch, q8, synth) -> int:
         q8.quant_8bit(x, aq, As, blk, EPS, -448.0, 448.0, False)
         big.fill_(1)  # evict: 256 MiB written between launches
         q8.blockwise_scaled_mm(aq, Wq, As, Ws, torch.bfloat16, block=(blk, blk), out=D)
-    # decode block32 GEMMs (N=4096, K=7168): M=1 (weight-streaming kernel) and
-    # M=16 (the kernel that stages the activations in LDS)
+    # decode block32 GEMMs (N=4096, K=7168): M=1 (four rows' block partials per
+    # MFMA), M=16 (activations staged in LDS once per workgroup) and M=64
+    # (split K: float32 partials in the workspace, then the fixed-order sum)
     Nd, db = 4096, 32
     Wd, Wsd = synth.fp8_block_weights(Nd, K, db, db, seed=0)
     Wd, Wsd = Wd.to(dev), Wsd.to(dev)
-    for Md in (1, 16):
+    for Md in (1, 16, 64):
         xd = synth.activations(Md, K, "bf16", outlier_frac=0.01, seed=0).to(dev)
         aqd = torch.empty((Md, K), dtype=torch.float8_e4m3fn, device=dev)
         Asd = torch.empty((Md, K // db), dtype=torch.float32, device=dev)
@@ -571,7 +572,7 @@ def traffic_probe(torch, q8, synth) -> int:
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    log("traffic probe done: 3 prefill GEMM launches, 3 decode GEMM launches each at M=1 and M=16, "
+    log("traffic probe done: 3 prefill GEMM launches, 3 decode GEMM launches each at M=1, 16 and 64, "
         "3 MoE grouped GEMM launches, 3 copies of 268435456 bytes")
     return 0
 

@@ -18,13 +18,19 @@
 //             four v_mfma_f32_16x16x32_fp8_fp8 per slab for 32-wide blocks.
 //             XCD-aware tile order. The grouped (MoE) variant walks
 //             (expert, n tile, m tile) with row gather/scatter maps.
-// gemm_skinny (M <= 64, decode; also the fallback when K is not a multiple of
-//             128, one 64-row block per grid row) streams W once: each workgroup owns 16 W rows,
-//             its waves split the K blocks, fragments are loaded straight
-//             from global memory into MFMA registers (W in the first operand
-//             slot, so a lane's four outputs share one activation row and
-//             one scale product), and the waves' float32 partials are summed
-//             in a fixed order through LDS (deterministic).
+// Decode (M <= 64) kernels stream W once, its fragments loaded straight from
+// global memory into MFMA registers (W in the first operand slot, so a lane's
+// four outputs share one activation row and one scale product), and sum the
+// waves' float32 partials in a fixed order through LDS (deterministic):
+// gemm_stream     one workgroup per 16 W rows, waves splitting the K chunks;
+// gemm_stream_pk  up to 8 rows, 32-wide blocks: four rows' block partials per
+//                 MFMA (column j of the activation operand is one row's block);
+// gemm_stream_sa  8..16 rows: the activation rows staged in LDS per workgroup;
+// gemm_split_mid  17..64 rows: K split into ranges, 64 W rows per workgroup,
+//                 the range's activation slice in LDS, float32 partials in the
+//                 caller's workspace, summed in order by gemm_split_reduce;
+// gemm_skinny     K not a multiple of 128 (8-byte fragments), one 64-row block
+//                 per grid row.
 #include <atomic>
 #include <type_traits>
 
