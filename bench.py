@@ -106,7 +106,7 @@ def measured_traffic(kernel: str, workload: str, sha: str):
 
 
 # ---------------------------------------------------------------------------
-def bench_prefill(torch, q8, synth, steps, warmup):
+def bench_prefill(torch, q8, synth, steps, warmup, ramp_ms):
     M, N, K, blk = 4096, 7168, 7168, 128
     dev = "cuda:0"
     x = synth.activations(M, K, "bf16", seed=0).to(dev)
@@ -128,6 +128,18 @@ def bench_prefill(torch, q8, synth, steps, warmup):
         else:
             q8.blockwise_scaled_mm(aq, Wq, As, Ws, torch.bfloat16, block=(blk, blk), out=D)
 
+    # Clock ramp: from idle the GPU needs ≈ 50 ms of back-to-back work before
+    # its clock settles (measured per GEMM launch from a cold start: ≈ 450 us
+    # in the first ten launches, 230 us after 15 ms, 204-206 us from ≈ 50 ms
+    # on). The step runs untimed for ramp_ms of wall time first, so that a
+    # short warm-up does not time the ramp; then the warm-up steps as asked.
+    ramp_steps = 0
+    t_r = time.perf_counter()
+    while (time.perf_counter() - t_r) * 1e3 < ramp_ms:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+        ramp_steps += 8
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -151,6 +163,7 @@ def bench_prefill(torch, q8, synth, steps, warmup):
         "gemm_tflops": flops / (g_us["mean"] * 1e-6) / 1e12,
         "shape": (M, N, K, blk),
         "x": x, "Wq": Wq, "Ws": Ws,
+        "clock_ramp": {"ms": ramp_ms, "steps": ramp_steps},
     }
 
 
@@ -609,6 +622,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--clock-ramp-ms", type=float, default=150.0,
+                    help="untimed prefill steps for this long before the warm-up steps (clock settling)")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="prefill rows for the oracle baseline")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run prefill GEMM launches and a 256 MiB device copy (for HBM counters)")
@@ -628,7 +643,7 @@ def main() -> int:
     log(f"device {torch.cuda.get_device_name(0)}")
     if args.traffic_probe:
         return traffic_probe(torch, q8, synth)
-    pre = bench_prefill(torch, q8, synth, args.steps, args.warmup)
+    pre = bench_prefill(torch, q8, synth, args.steps, args.warmup, args.clock_ramp_ms)
     log(f"prefill: {pre['ms_per_step']:.3f} ms/step, GEMM {pre['gemm_us']['mean']:.1f} us "
         f"= {pre['gemm_tflops']:.0f} TFLOP/s")
     M, N, K, blk = pre["shape"]
@@ -665,6 +680,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_ramp": pre["clock_ramp"],
         "ms_per_step": round(pre["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",

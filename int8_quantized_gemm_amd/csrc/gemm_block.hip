@@ -1149,21 +1149,47 @@ void gemm_split_mid(TileParams p, float* __restrict__ part, int Kc) {
   {
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (uint32_t)(M * K));
     const __amdgpu_buffer_rsrc_t rS = make_rsrc(p.As, (uint32_t)(M * KB * 4));
+    // Piece pc = 64 i + lane of the slice is (row, j) = divmod(pc, pr); a
+    // lane's pieces advance by 64 kMidNW per step, so (row, j) is stepped by
+    // the constant quotient and remainder of that stride with one carry
+    // instead of a division per piece (likewise for the scales).
     const int pieces = (int)M * pr;
-    for (int i = w; i * 64 < pieces; i += kMidNW) {
-      const int pc = i * 64 + lane;
-      const int row = pc / pr, j = pc - row * pr;
-      // slot (row, j) holds piece j ^ key(row); lanes past the slice read
-      // zeros (offset beyond the resource) into the padding
-      const uint32_t src = pc < pieces ? (uint32_t)(row * K + k0 + 16 * (j ^ (row & 15))) : 0xFFFFFFF0u;
-      b2l16(rA, src, 0, sA + i * 1024);
+    {
+      constexpr int kStride = 64 * kMidNW;
+      const int dq = kStride / pr, dr = kStride - dq * pr;
+      int pc = w * 64 + lane;
+      int row = pc / pr, j = pc - row * pr;
+      for (int i = w; i * 64 < pieces; i += kMidNW) {
+        // slot (row, j) holds piece j ^ key(row); lanes past the slice read
+        // zeros (offset beyond the resource) into the padding
+        const uint32_t src = pc < pieces ? (uint32_t)(row * K + k0 + 16 * (j ^ (row & 15))) : 0xFFFFFFF0u;
+        b2l16(rA, src, 0, sA + i * 1024);
+        pc += kStride;
+        row += dq;
+        j += dr;
+        if (j >= pr) {
+          j -= pr;
+          ++row;
+        }
+      }
     }
     const int nsc = (int)M * kbc;
-    for (int i = w; i * 64 < nsc; i += kMidNW) {
-      const int f = i * 64 + lane;
-      const int row = f / kbc, c = f - row * kbc;
-      const uint32_t src = f < nsc ? (uint32_t)((row * KB + kb0 + c) * 4) : 0xFFFFFFF0u;
-      b2l4(rS, src, 0, sS + i * 64);
+    {
+      constexpr int kStride = 64 * kMidNW;
+      const int dq = kStride / kbc, dr = kStride - dq * kbc;
+      int f = w * 64 + lane;
+      int row = f / kbc, c = f - row * kbc;
+      for (int i = w; i * 64 < nsc; i += kMidNW) {
+        const uint32_t src = f < nsc ? (uint32_t)((row * KB + kb0 + c) * 4) : 0xFFFFFFF0u;
+        b2l4(rS, src, 0, sS + i * 64);
+        f += kStride;
+        row += dq;
+        c += dr;
+        if (c >= kbc) {
+          c -= kbc;
+          ++row;
+        }
+      }
     }
   }
   // ---- this wave's weight chunks (row block rb, chunks h, h + NP, ...), all
