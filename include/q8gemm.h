@@ -169,11 +169,19 @@ int blockwise_scaled_mm(const void* A, const float* As, const void* W, const flo
  * M >= 0, N >= 1; As and Ws 4-byte aligned; A and W each below 4 GiB.
  * Byte 255 (NaN) is not a valid scale (documented, not checked).
  * Accumulation: FP8 products scaled and summed in float32 inside the matrix
- * cores (order unspecified). Caller owns all buffers; asynchronous on stream.
+ * cores (order unspecified); for 17..64 rows with a workspace, K is split into
+ * ranges whose float32 partials are summed in ascending range order.
+ * workspace: blockwise_scaled_mm_e8m0_workspace_size() bytes, 16-byte
+ * aligned: the split-K partials (S x M x N floats; 4 MiB for 64 x 4096 x
+ * 7168), 0 for every other shape (then NULL is allowed). Q8_EWORKSPACE if it
+ * is needed and missing or short. The contents need no initialisation and are
+ * overwritten. Caller owns all buffers; asynchronous on stream.
  */
+size_t blockwise_scaled_mm_e8m0_workspace_size(int64_t M, int64_t N, int64_t K, int bn);
 int blockwise_scaled_mm_e8m0(const void* A, const uint8_t* As, const void* W, const uint8_t* Ws,
                              const void* bias, void* D, q8_dtype out_dtype,
-                             int64_t M, int64_t N, int64_t K, int bn, hipStream_t stream);
+                             int64_t M, int64_t N, int64_t K, int bn,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * INT8 W8A8 scaled GEMM.

@@ -40,7 +40,7 @@ EXPORTS = (
     "q8gemm_last_error",
     "quant_8bit_workspace_size", "quant_8bit",
     "blockwise_scaled_mm_workspace_size", "blockwise_scaled_mm",
-    "blockwise_scaled_mm_e8m0",
+    "blockwise_scaled_mm_e8m0_workspace_size", "blockwise_scaled_mm_e8m0",
     "scaled_mm_int8",
     "scaled_mm_fp8",
     "moe_finalize",
@@ -66,7 +66,9 @@ _quant = _sig("quant_8bit", _i, _p, _i, _i64, _i64, _i64, _p, _i, _p, _i64, _i, 
 _bmm_ws = _sig("blockwise_scaled_mm_workspace_size", _sz, _i64, _i64, _i64, _i, _i)
 _bmm = _sig("blockwise_scaled_mm", _i, _p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i, _i, _p,
             _sz, _p)
-_bmm8 = _sig("blockwise_scaled_mm_e8m0", _i, _p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i, _p)
+_bmm8_ws = _sig("blockwise_scaled_mm_e8m0_workspace_size", _sz, _i64, _i64, _i64, _i)
+_bmm8 = _sig("blockwise_scaled_mm_e8m0", _i, _p, _p, _p, _p, _p, _p, _i, _i64, _i64, _i64, _i, _p,
+             _sz, _p)
 _imm = _sig("scaled_mm_int8", _i, _p, _p, _i64, _p, _p, _i64, _p, _p, _i, _i64, _i64, _i64, _p)
 _fin = _sig("moe_finalize", _i, _p, _i, _p, _p, _i64, _i, _i64, _p, _p)
 _fmm = _sig("scaled_mm_fp8", _i, _p, _p, _i64, _p, _p, _i64, _p, _p, _i, _i64, _i64, _i64, _p)
@@ -313,8 +315,9 @@ def blockwise_scaled_mm_e8m0(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a:
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=dev)
     _contig(out)
+    ws, wsb = _workspace(dev, _ws_size(_bmm8_ws, M, N, K, block_n))
     _check(_bmm8(_ptr(mat_a), _ptr(scales_a), _ptr(mat_b), _ptr(scales_b), _ptr(bias), _ptr(out),
-                 _dt(out.dtype), M, N, K, block_n, _stream(dev)))
+                 _dt(out.dtype), M, N, K, block_n, ws, wsb, _stream(dev)))
     return out
 
 

@@ -145,9 +145,15 @@ int blockwise_scaled_mm(const void* A, const float* As, const void* W, const flo
   return hip_status(q8::launch_blockwise(a, stream), fn);
 }
 
+size_t blockwise_scaled_mm_e8m0_workspace_size(int64_t M, int64_t N, int64_t K, int bn) {
+  if (M < 0 || N < 1 || K < 1 || bn < 16 || bn % 16 != 0 || K % 128 != 0) return 0;
+  return q8::blockwise_e8m0_workspace_bytes(M, N, K);
+}
+
 int blockwise_scaled_mm_e8m0(const void* A, const uint8_t* As, const void* W, const uint8_t* Ws,
                              const void* bias, void* D, q8_dtype out_dtype, int64_t M, int64_t N,
-                             int64_t K, int bn, hipStream_t stream) {
+                             int64_t K, int bn, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
   static const char* fn = "blockwise_scaled_mm_e8m0";
   if (!is_16bit_out(out_dtype)) return fail(Q8_EINVAL, "%s: out_dtype must be BF16 or F16", fn);
   if (M < 0 || N < 1 || K < 1) return fail(Q8_ESHAPE, "%s: need M >= 0, N >= 1, K >= 1", fn);
@@ -161,8 +167,13 @@ int blockwise_scaled_mm_e8m0(const void* A, const uint8_t* As, const void* W, co
   if (!A || !As || !W || !Ws || !D) return fail(Q8_EINVAL, "%s: null pointer", fn);
   if ((uintptr_t)As % 4 != 0 || (uintptr_t)Ws % 4 != 0)
     return fail(Q8_EINVAL, "%s: As and Ws must be 4-byte aligned", fn);
+  const size_t need = blockwise_scaled_mm_e8m0_workspace_size(M, N, K, bn);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(Q8_EWORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  if (need && (uintptr_t)workspace % 16 != 0)
+    return fail(Q8_EINVAL, "%s: workspace must be 16-byte aligned", fn);
   q8::MxGemmArgs a{static_cast<const uint8_t*>(A), As, static_cast<const uint8_t*>(W), Ws,
-                   bias, D, out_dtype, M, N, K, bn};
+                   bias, D, out_dtype, M, N, K, bn, need ? workspace : nullptr};
   return hip_status(q8::launch_blockwise_e8m0(a, stream), fn);
 }
 

@@ -30,6 +30,13 @@
 // gemm_stream_mx (M <= 64) streams W once, one workgroup per 16 weight rows,
 //                lane group g loading bytes [16g, 16g + 16) and
 //                [64 + 16g, 64 + 16g + 16) of each 128-byte chunk.
+// gemm_split_mx  (17 <= M <= 64, with a workspace) K split into ranges: a
+//                workgroup owns 64 weight rows of one range, copies the range's
+//                activation slice and its scale dwords into LDS once, streams
+//                its weights, and writes float32 partials that
+//                gemm_split_reduce_mx sums over the ranges in a fixed order.
+#include <atomic>
+
 #include "q8_internal.h"
 #include "tile_common.h"
 
@@ -327,6 +334,239 @@ __global__ __launch_bounds__(NW * 64) void gemm_stream_mx(MxParams p) {
   }
 }
 
+// ---- split K for 17..64 rows ---------------------------------------------------
+constexpr int kMxMidRows = 64;  // weight rows per workgroup (four 16-row blocks)
+constexpr int kMxMidNW = 8;     // waves: four row blocks x two chunk parities
+
+// Workgroup (n block of 64 weight rows, K range s): all waves copy the range's
+// activation slice (M rows x Kc bytes, 16-byte pieces, piece j of row m at
+// slot j ^ (m & 15), so that the sixteen rows of a fragment read hit distinct
+// banks) and the rows' scale dwords (four 32-wide blocks per 128-byte chunk)
+// into LDS, then issue every weight load of their chunks (row block w & 3,
+// chunks of parity w >> 2) before waiting for the copies. Each chunk and
+// 16-row activation block is one MX-scaled MFMA accumulating across K (block
+// scales applied in the matrix core); the two parities' sums meet in LDS and
+// one float32 partial per output goes to part[s][m][n].
+template <int MT, int R>
+__global__ __launch_bounds__(kMxMidNW * 64) void gemm_split_mx(MxParams p, float* __restrict__ part, int Kc) {
+  constexpr int NP = kMxMidNW / 4;
+  static_assert(NP == 2 && R <= 64, "two chunk parities; a wave's scale dwords fit one register");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rb = w & 3, h = w >> 2;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t N = p.N, K = p.K, M = p.M;
+  const int KB = p.KB;
+  const int s_idx = blockIdx.y;
+  const int64_t k0 = (int64_t)s_idx * Kc;
+  const int ncc = Kc / 128;  // chunks in the range
+  const int pr = Kc / 16;    // 16-byte pieces per activation row
+  const int64_t n0 = (int64_t)blockIdx.x * kMxMidRows;
+  uint8_t* sA = smem;
+  const uint32_t a_bytes = (uint32_t)(((M * Kc) + 1023) & ~1023LL);
+  uint32_t* sS = reinterpret_cast<uint32_t*>(smem + a_bytes);  // [M][ncc] scale dwords
+
+  {
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, p.a_bytes);
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(p.As, p.as_bytes);
+    constexpr int kStride = 64 * kMxMidNW;
+    // piece pc = 64 i + lane is (row, j) = divmod(pc, pr), stepped by the
+    // stride's quotient and remainder with one carry (no division per piece)
+    const int pieces = (int)M * pr;
+    {
+      const int dq = kStride / pr, dr = kStride - dq * pr;
+      int pc = w * 64 + lane;
+      int row = pc / pr, j = pc - row * pr;
+      for (int i = w; i * 64 < pieces; i += kMxMidNW) {
+        const uint32_t src = pc < pieces ? (uint32_t)(row * K + k0 + 16 * (j ^ (row & 15))) : 0xFFFFFFF0u;
+        b2l16(rA, src, 0, sA + i * 1024);
+        pc += kStride;
+        row += dq;
+        j += dr;
+        if (j >= pr) {
+          j -= pr;
+          ++row;
+        }
+      }
+    }
+    // scale dword (row, c): bytes kb0 + 4c .. kb0 + 4c + 3 of the row
+    const int nsd = (int)M * ncc;
+    {
+      const int dq = kStride / ncc, dr = kStride - dq * ncc;
+      int f = w * 64 + lane;
+      int row = f / ncc, c = f - row * ncc;
+      for (int i = w; i * 64 < nsd; i += kMxMidNW) {
+        const uint32_t src = f < nsd ? (uint32_t)(row * KB + k0 / 32 + 4 * c) : 0xFFFFFFF0u;
+        b2l4(rS, src, 0, sS + i * 64);
+        f += kStride;
+        row += dq;
+        c += dr;
+        if (c >= ncc) {
+          c -= ncc;
+          ++row;
+        }
+      }
+    }
+  }
+  // the wave's weight rows and their scale dwords (row block rb shares one
+  // weight-scale row: bn is a multiple of 16); lane u holds the dword of the
+  // wave's u-th chunk
+  const int64_t nrow = n0 + 16 * rb + r16 < N ? n0 + 16 * rb + r16 : N - 1;
+  const uint8_t* wp = p.W + nrow * K + k0 + 16 * g;
+  int64_t nb = (n0 + 16 * rb) / p.bn;
+  if (nb > p.nbw - 1) nb = p.nbw - 1;
+  const int li = lane < R ? lane : R - 1;
+  const int lc = h + li * NP < ncc ? h + li * NP : ncc - 1;
+  const uint32_t wsl = reinterpret_cast<const uint32_t*>(p.Ws + nb * KB + k0 / 32)[lc];
+  asm volatile("" ::: "memory");
+  i32x8 wf[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int cc0 = h + u * NP;
+    const int cc = cc0 < ncc ? cc0 : ncc - 1;
+    wf[u] = gload_mx(wp + (int64_t)cc * 128);
+  }
+  // loads complete in order: with at most 2R (weight halves) + 1 (scale
+  // dword) outstanding, this wave's copies have landed; the barrier carries
+  // no fence, so the weight loads stay in flight across it
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * R + 1) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // LDS offsets of this lane's pieces for its first chunk (h), per 16-row
+  // block t; chunk h + NP u adds 256 u bytes (see the float32-scale kernel)
+  uint32_t aoff[MT][2], soff[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = 16 * t + r16 < M ? 16 * t + r16 : (int)M - 1;
+    const int key = m & 15;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) aoff[t][f] = (uint32_t)(m * Kc + 16 * ((8 * h + 4 * f + g) ^ key));
+    soff[t] = (uint32_t)((m * ncc + h) * 4);
+  }
+  const uint8_t* sSb = reinterpret_cast<const uint8_t*>(sS);
+  f32x4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int cc = h + u * NP;
+    if (cc >= ncc) break;
+    const uint32_t ws = (uint32_t)__builtin_amdgcn_readlane((int)wsl, u) >> (8 * g);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(sA + aoff[t][0] + 256 * u);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(sA + aoff[t][1] + 256 * u);
+      const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const uint32_t as = *reinterpret_cast<const uint32_t*>(sSb + soff[t] + 8 * u) >> (8 * g);
+      acc[t] = mfma_mx(wf[u], af, acc[t], ws, as);
+    }
+  }
+  __syncthreads();  // every wave is done with the slice
+  f32x4* red = reinterpret_cast<f32x4*>(smem);  // [kMxMidNW][MT][64]
+#pragma unroll
+  for (int t = 0; t < MT; ++t) red[(w * MT + t) * 64 + lane] = acc[t];
+  __syncthreads();
+  if (h == 0) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      f32x4 v = red[(rb * MT + t) * 64 + lane];
+#pragma unroll
+      for (int hh = 1; hh < NP; ++hh) v += red[((rb + 4 * hh) * MT + t) * 64 + lane];
+      const int64_t m = 16 * t + r16;
+      const int64_t n = n0 + 16 * rb + 4 * g;
+      if (m < M && n < N) *reinterpret_cast<f32x4*>(part + ((int64_t)s_idx * M + m) * N + n) = v;
+    }
+  }
+}
+
+// D[m, n .. n+3] = sum_s part[s][m][n .. n+3] (s ascending) + bias, rounded.
+__global__ __launch_bounds__(256) void gemm_split_reduce_mx(MxParams p, const float* __restrict__ part,
+                                                            int S) {
+  const int64_t N = p.N, M = p.M;
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nv = N / 4;
+  if (v >= M * nv) return;
+  const int64_t m = v / nv, n = (v - m * nv) * 4;
+  f32x4 sum = *reinterpret_cast<const f32x4*>(part + m * N + n);
+  for (int s = 1; s < S; ++s) sum += *reinterpret_cast<const f32x4*>(part + ((int64_t)s * M + m) * N + n);
+  const bool bf16 = p.out_bf16 != 0, vec = p.d_vec4 != 0;
+  store4_mx(p, m, n, p.bias ? sum + load_bias4(p.bias, n, N, bf16, vec) : sum, bf16, vec);
+}
+
+struct MxMidPlan {
+  int S = 0, Kc = 0, mt = 0, R = 0;
+  int64_t lds = 0;
+};
+
+// K ranges: the fewest that give 256 workgroups, each a multiple of 256 bytes
+// and at most 2048 (a wave's chunks then fit its registers); none fits -> not
+// this kernel.
+bool mx_mid_plan(int64_t M, int64_t N, int64_t K, MxMidPlan& pl) {
+  if (M < 17 || M > 64 || N % 4 != 0) return false;
+  const int64_t groups = (N + kMxMidRows - 1) / kMxMidRows;
+  int best = 0;
+  for (int S = 1; S <= 32; S *= 2) {
+    if (K % (256LL * S) != 0 || K / S > 2048) continue;
+    best = S;
+    if (groups * S >= 256) break;
+  }
+  if (!best || groups * best > 0x7FFFFFFFLL) return false;
+  pl.S = best;
+  pl.Kc = (int)(K / best);
+  const int ncc = pl.Kc / 128;
+  pl.R = (ncc + 1) / 2 <= 4 ? 4 : 8;
+  pl.mt = (int)((M + 15) / 16);
+  const int64_t a_bytes = ((M * pl.Kc) + 1023) & ~1023LL;
+  const int64_t s_bytes = ((M * ncc + 63) / 64) * 64 * 4;
+  const int64_t red_bytes = (int64_t)kMxMidNW * pl.mt * 64 * 16;
+  pl.lds = a_bytes + s_bytes > red_bytes ? a_bytes + s_bytes : red_bytes;
+  return pl.lds <= 160 * 1024;
+}
+
+// dynamic LDS above 64 KiB needs the kernel's limit raised, once per device
+hipError_t raise_lds_limit_mx(const void* kern, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  const uint64_t bit = 1ull << dev;
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
+template <int MT, int R>
+hipError_t launch_split_mx_inst(const MxParams& p, const MxMidPlan& pl, float* part, hipStream_t st) {
+  const auto kern = gemm_split_mx<MT, R>;
+  static std::atomic<uint64_t> lds_raised{0};
+  hipError_t e = raise_lds_limit_mx(reinterpret_cast<const void*>(kern), lds_raised);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((p.N + kMxMidRows - 1) / kMxMidRows), (unsigned)pl.S);
+  hipLaunchKernelGGL(kern, grid, dim3(kMxMidNW * 64), (unsigned)pl.lds, st, p, part, pl.Kc);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t vecs = p.M * (p.N / 4);
+  hipLaunchKernelGGL(gemm_split_reduce_mx, dim3((unsigned)((vecs + 255) / 256)), dim3(256), 0, st, p,
+                     (const float*)part, pl.S);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_split_mx_r(const MxParams& p, const MxMidPlan& pl, float* part, hipStream_t st) {
+  return pl.R == 4 ? launch_split_mx_inst<MT, 4>(p, pl, part, st) : launch_split_mx_inst<MT, 8>(p, pl, part, st);
+}
+
+hipError_t launch_split_mx(const MxParams& p, const MxMidPlan& pl, float* part, hipStream_t st) {
+  switch (pl.mt) {
+    case 2: return launch_split_mx_r<2>(p, pl, part, st);
+    case 3: return launch_split_mx_r<3>(p, pl, part, st);
+    default: return launch_split_mx_r<4>(p, pl, part, st);
+  }
+}
+
 constexpr int kMxBM = 256, kMxBN = 256, kMxWM = 2, kMxWN = 4;
 constexpr int kMxStreamNW = 16;
 
@@ -339,6 +579,13 @@ hipError_t launch_stream_mx(const MxParams& p, hipStream_t st) {
 }
 
 }  // namespace
+
+size_t blockwise_e8m0_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (K % 128 != 0) return 0;
+  MxMidPlan pl;
+  if (!mx_mid_plan(M, N, K, pl)) return 0;
+  return (size_t)pl.S * (size_t)M * (size_t)N * sizeof(float);
+}
 
 hipError_t launch_blockwise_e8m0(const MxGemmArgs& a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
@@ -355,6 +602,11 @@ hipError_t launch_blockwise_e8m0(const MxGemmArgs& a, hipStream_t st) {
   p.tiles_m = (a.M + kMxBM - 1) / kMxBM;
   p.tiles_n = (a.N + kMxBN - 1) / kMxBN;
   if (a.M <= 64) {
+    // 17..64 rows: split K, partials in the workspace
+    MxMidPlan pl;
+    if (mx_mid_plan(a.M, a.N, a.K, pl) && a.workspace && (uintptr_t)a.workspace % 16 == 0 &&
+        (uintptr_t)a.A % 16 == 0)
+      return launch_split_mx(p, pl, static_cast<float*>(a.workspace), st);
     const int mt = (int)((a.M + 15) / 16);
     switch (mt) {
       case 1: return launch_stream_mx<1>(p, st);

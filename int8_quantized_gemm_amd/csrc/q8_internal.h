@@ -48,7 +48,10 @@ struct MxGemmArgs {
   const uint8_t* A; const uint8_t* As; const uint8_t* W; const uint8_t* Ws;
   const void* bias; void* D; q8_dtype out_dtype;
   int64_t M, N, K; int bn;
+  void* workspace;  // split-K partials (17..64 rows), or null
 };
+// workspace bytes the E8M0 call needs for this shape (0: none)
+size_t blockwise_e8m0_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_blockwise_e8m0(const MxGemmArgs& a, hipStream_t stream);
 
 // ---- INT8 GEMM ----------------------------------------------------------------

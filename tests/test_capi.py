@@ -170,7 +170,7 @@ def test_moe_and_grouped_validation(q8):
 
 def test_e8m0_gemm_validation(q8):
     p = None
-    args = lambda M, N, K, bn, out=q8.Q8_BF16, ptr=p: (ptr, ptr, ptr, ptr, p, ptr, out, M, N, K, bn, p)
+    args = lambda M, N, K, bn, out=q8.Q8_BF16, ptr=p: (ptr, ptr, ptr, ptr, p, ptr, out, M, N, K, bn, p, 0, p)
     assert q8._bmm8(*args(4, 256, 500, 32)) == q8.Q8_ESHAPE            # K not a multiple of 128
     assert "multiple of 128" in q8.last_error()
     assert q8._bmm8(*args(4, 256, 512, 24)) == q8.Q8_EUNSUPPORTED      # bn not a multiple of 16
@@ -179,10 +179,20 @@ def test_e8m0_gemm_validation(q8):
     assert q8._bmm8(*args(4, 256, 512, 32)) == q8.Q8_EINVAL            # null pointers
     assert q8._bmm8(*args(0, 256, 512, 32)) == q8.Q8_OK                # M = 0: no-op
     # scale tables must be 4-byte aligned (the kernels read scale dwords)
-    assert q8._bmm8(16, 18, 16, 16, p, 16, q8.Q8_BF16, 4, 256, 512, 32, p) == q8.Q8_EINVAL
+    assert q8._bmm8(16, 18, 16, 16, p, 16, q8.Q8_BF16, 4, 256, 512, 32, p, 0, p) == q8.Q8_EINVAL
     assert "aligned" in q8.last_error()
     # A beyond 4 GiB
     assert q8._bmm8(*args(1 << 20, 256, 1 << 12, 32)) == q8.Q8_EUNSUPPORTED
+    # 17..64 rows split K: float32 partials of 4 ranges in the workspace
+    assert q8._bmm8_ws(64, 4096, 7168, 32) == 4 * 64 * 4096 * 4
+    assert q8._bmm8_ws(17, 1000, 1024, 32) == 4 * 17 * 1000 * 4
+    for M, N in ((16, 4096), (65, 4096), (33, 1002)):
+        assert q8._bmm8_ws(M, N, 7168, 32) == 0
+    wargs = lambda ws, wsb: (16, 16, 16, 16, p, 16, q8.Q8_BF16, 33, 4096, 7168, 32, ws, wsb, p)
+    assert q8._bmm8(*wargs(p, 0)) == q8.Q8_EWORKSPACE
+    assert q8._bmm8(*wargs(32, 4 * 33 * 4096 * 4 - 1)) == q8.Q8_EWORKSPACE
+    assert q8._bmm8(*wargs(40, 4 * 33 * 4096 * 4)) == q8.Q8_EINVAL      # misaligned
+    assert "aligned" in q8.last_error()
 
 
 def test_quant_scale_ue8m0_range(q8):
