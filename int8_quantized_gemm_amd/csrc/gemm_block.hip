@@ -1109,10 +1109,10 @@ void gemm_stream_sa(TileParams p) {
 // front), and writes its float32 partial [M, 64] for that K range;
 // gemm_split_reduce then sums the S partials of every output in a fixed
 // order (deterministic), adds the bias and rounds.
-// MFMA columns: for 128-wide K blocks, sixteen activation rows (one MFMA per
-// chunk and 16-row block); for 32-wide blocks, (row, block) pairs packed as
-// in gemm_stream_pk (four rows x four blocks per MFMA), so each MFMA's
-// partials are already per block and one scale product serves a lane.
+// MFMA columns: sixteen activation rows per MFMA (one per chunk and 16-row
+// block for 128-wide K blocks; for 32-wide blocks one per chunk, block and
+// 16-row block, each taking a single block through the scale selector of
+// mfma_block), so a lane's four outputs share one scale product.
 // LDS activation slice: dense [M, Kc], 16-byte piece j of row m stored at
 // piece position j ^ (m & 15) (Kc a multiple of 256 bytes keeps every row's
 // pieces inside the row); sixteen lanes reading one piece of sixteen rows

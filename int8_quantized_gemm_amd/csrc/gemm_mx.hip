@@ -30,6 +30,11 @@
 // gemm_stream_mx (M <= 64) streams W once, one workgroup per 16 weight rows,
 //                lane group g loading bytes [16g, 16g + 16) and
 //                [64 + 16g, 64 + 16g + 16) of each 128-byte chunk.
+// gemm_stream_mx_sa (M <= 16, K a multiple of 1024) as gemm_stream_mx, with
+//                the activation rows and their scale bytes copied into LDS
+//                once per workgroup instead of read from L2 by every wave
+//                (measured against reading them per wave: M = 1 7.90 -> 7.62,
+//                M = 4 8.94 -> 7.97, M = 16 11.7 -> 9.1 us at N=4096, K=7168).
 // gemm_split_mx  (17 <= M <= 64, with a workspace) K split into ranges: a
 //                workgroup owns 64 weight rows of one range, copies the range's
 //                activation slice and its scale dwords into LDS once, streams
@@ -334,6 +339,103 @@ __global__ __launch_bounds__(NW * 64) void gemm_stream_mx(MxParams p) {
   }
 }
 
+// ---- up to 16 rows: activations staged in LDS once per workgroup ---------------
+constexpr int kMxSaNW = 16, kMxSaR = 4;
+
+// dynamic LDS: activation rows (pitch K + 16), scale bytes rounded up to whole
+// 1 KB copies, and the waves' partials
+inline int64_t stream_mx_sa_lds(int64_t M, int64_t K) {
+  return M * (K + 16) + ((M * (K / 32) + 1023) & ~1023LL) + (int64_t)kMxSaNW * 64 * 16;
+}
+
+inline bool stream_mx_sa_fits(int64_t M, int64_t K) {
+  return M >= 1 && M <= 16 && K % 1024 == 0 && (K / 128 + kMxSaNW - 1) / kMxSaNW <= kMxSaR &&
+         stream_mx_sa_lds(M, K) <= 160 * 1024;
+}
+
+// One workgroup per 16 weight rows; its waves split the 128-byte K chunks.
+// The activation rows and their scale bytes are copied into LDS first
+// (buffer->LDS, 1 KB per wave instruction), then each wave issues its weight
+// loads and waits for its copies with vmcnt(2R + 1) and a barrier without a
+// fence, so the weight loads stay in flight across it. One MX-scaled MFMA per
+// chunk (sixteen activation rows), partials summed over the waves in a fixed
+// order.
+template <int NW, int R>
+__global__ __launch_bounds__(NW * 64) void gemm_stream_mx_sa(MxParams p) {
+  static_assert(R <= 64, "a wave's weight-scale dwords fit one register");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t N = p.N, K = p.K, M = p.M;  // M <= 16
+  const int KB = p.KB;                      // scale bytes per row
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int NC = (int)(K / 128);
+  const int c_b = (int)((int64_t)w * NC / NW), c_e = (int)((int64_t)(w + 1) * NC / NW);
+  const uint32_t a_pitch = (uint32_t)K + 16;
+  const uint32_t s_bytes = (uint32_t)(M * KB);
+  uint8_t* sA = smem;
+  uint8_t* sS = smem + M * a_pitch;
+  f32x4* red = reinterpret_cast<f32x4*>(sS + ((s_bytes + 1023u) & ~1023u));  // [NW][64]
+  {
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, p.a_bytes);
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(p.As, s_bytes);
+    const int per_row = (int)(K / 1024), a_loads = (int)M * per_row;
+    for (int i = w; i < a_loads; i += NW) {
+      const int row = i / per_row, col = (i - row * per_row) * 1024;
+      b2l16(rA, (uint32_t)lane * 16, (uint32_t)i * 1024, sA + row * a_pitch + col);
+    }
+    // the tail of the last 1 KB reads zeros from the resource's range check
+    const int s_loads = (int)((s_bytes + 1023u) >> 10);
+    for (int i = w; i < s_loads; i += NW) b2l16(rS, (uint32_t)lane * 16, (uint32_t)i * 1024, sS + i * 1024);
+  }
+  // the wave's weight-scale dwords (lane u: chunk c_b + u; the 16 rows share
+  // one scale row since n0 and bn are multiples of 16) and weight chunks,
+  // issued after the copies (clamped, so exactly 2R loads follow the dword)
+  const int64_t nrow = n0 + r16 < N ? n0 + r16 : N - 1;
+  const uint8_t* wp = p.W + nrow * K + 16 * g;
+  const int wc = c_b + lane < NC ? c_b + lane : NC - 1;
+  const uint32_t wsl = reinterpret_cast<const uint32_t*>(p.Ws + (nrow / p.bn) * KB)[wc];
+  asm volatile("" ::: "memory");
+  i32x8 wf[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int c = c_b + u < NC - 1 ? c_b + u : NC - 1;
+    wf[u] = gload_mx(wp + (int64_t)c * 128);
+  }
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * R + 1) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int arow = r16 < M ? r16 : (int)M - 1;  // rows past M repeat the last (never stored)
+  const uint8_t* al = sA + arow * a_pitch + 16 * g;
+  const uint8_t* sl = sS + arow * KB;
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int c = c_b + u;
+    if (c >= c_e) break;
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(al + c * 128);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(al + c * 128 + 64);
+    const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const uint32_t as = *reinterpret_cast<const uint32_t*>(sl + 4 * c) >> (8 * g);
+    const uint32_t ws = (uint32_t)__builtin_amdgcn_readlane((int)wsl, u) >> (8 * g);
+    acc = mfma_mx(wf[u], af, acc, ws, as);
+  }
+  red[w * 64 + lane] = acc;
+  __syncthreads();
+  const bool bf16 = p.out_bf16 != 0, vec = p.d_vec4 != 0;
+  for (int idx = tid; idx < 64; idx += NW * 64) {
+    const int64_t m = idx & 15;
+    if (m >= M) continue;
+    f32x4 sum = red[idx];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) sum += red[ww * 64 + idx];
+    const int64_t n = n0 + 4 * (idx >> 4);
+    if (n < N) store4_mx(p, m, n, p.bias ? sum + load_bias4(p.bias, n, N, bf16, vec && n + 3 < N) : sum, bf16, vec);
+  }
+}
+
 // ---- split K for 17..64 rows ---------------------------------------------------
 constexpr int kMxMidRows = 64;  // weight rows per workgroup (four 16-row blocks)
 constexpr int kMxMidNW = 8;     // waves: four row blocks x two chunk parities
@@ -554,6 +656,17 @@ hipError_t launch_split_mx_inst(const MxParams& p, const MxMidPlan& pl, float* p
   return hipGetLastError();
 }
 
+hipError_t launch_stream_mx_sa(const MxParams& p, hipStream_t st) {
+  const auto kern = gemm_stream_mx_sa<kMxSaNW, kMxSaR>;
+  static std::atomic<uint64_t> lds_raised{0};
+  const hipError_t e = raise_lds_limit_mx(reinterpret_cast<const void*>(kern), lds_raised);
+  if (e != hipSuccess) return e;
+  if ((p.N + 15) / 16 > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kern, dim3((unsigned)((p.N + 15) / 16)), dim3(kMxSaNW * 64),
+                     (unsigned)stream_mx_sa_lds(p.M, p.K), st, p);
+  return hipGetLastError();
+}
+
 template <int MT>
 hipError_t launch_split_mx_r(const MxParams& p, const MxMidPlan& pl, float* part, hipStream_t st) {
   return pl.R == 4 ? launch_split_mx_inst<MT, 4>(p, pl, part, st) : launch_split_mx_inst<MT, 8>(p, pl, part, st);
@@ -607,6 +720,9 @@ hipError_t launch_blockwise_e8m0(const MxGemmArgs& a, hipStream_t st) {
     if (mx_mid_plan(a.M, a.N, a.K, pl) && a.workspace && (uintptr_t)a.workspace % 16 == 0 &&
         (uintptr_t)a.A % 16 == 0)
       return launch_split_mx(p, pl, static_cast<float*>(a.workspace), st);
+    // up to 16 rows: the activations staged in LDS once per workgroup
+    if (stream_mx_sa_fits(a.M, a.K) && (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.As % 16 == 0)
+      return launch_stream_mx_sa(p, st);
     const int mt = (int)((a.M + 15) / 16);
     switch (mt) {
       case 1: return launch_stream_mx<1>(p, st);

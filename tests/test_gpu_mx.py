@@ -36,7 +36,7 @@ def test_quant_packed_e8m0(M, K):
 
 
 @pytest.mark.parametrize("M,N,K,bn,bias", [
-    (1, 256, 512, 32, False),      # streaming kernel, one row block
+    (1, 256, 512, 32, False),      # K not a multiple of 1024: streaming kernel, one row block
     (4, 4096, 1024, 32, True),
     (37, 200, 1024, 32, False),    # three row blocks, ragged N (17..64 rows: split K)
     (64, 512, 2048, 128, True),
@@ -44,6 +44,9 @@ def test_quant_packed_e8m0(M, K):
     (48, 1000, 2048, 64, True),    # split K, bn 64, ragged 64-row weight groups
     (33, 16, 4096, 32, False),     # split K, one weight group of 16 rows
     (20, 1002, 1024, 32, True),    # N not a multiple of 4: the streaming kernel
+    (12, 520, 2048, 32, True),     # up to 16 rows: activations staged in LDS, ragged N
+    (3, 300, 1024, 32, False),     # staged, three rows
+    (9, 48, 3072, 16, False),      # staged, bn 16, three weight-row blocks
     (65, 256, 512, 32, False),     # tile kernel from 65 rows
     (300, 520, 1024, 128, True),   # ragged M and N tiles
     (513, 768, 2048, 32, False),
