@@ -8,9 +8,11 @@
  *   tensor's data_ptr), unless a comment says otherwise. The caller owns and
  *   allocates every buffer, outputs and workspace included; outputs are
  *   written in place. The library never allocates or frees memory and may be
- *   called from several threads at once. Its only process-wide state is a
- *   per-device record that a kernel's LDS limit was raised (set once,
- *   thread-safe).
+ *   called from several threads at once. Its process-wide state: per-device
+ *   records that a kernel's LDS limit was raised, and, for the one
+ *   allocation-free entry point (moe_mm_data_noalloc), a fixed device array
+ *   per GPU and its device address, looked up once per device; each is set
+ *   once and thread-safe.
  * - Every matrix is row-major and contiguous unless a leading dimension is
  *   passed. Weights are [N, K] with K contiguous (the "nt" layout: a
  *   column-major [K, N] weight is the same bytes).
