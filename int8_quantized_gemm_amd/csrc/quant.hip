@@ -18,9 +18,13 @@
 //                      loads 8 consecutive elements (16 B for bf16/f16), the
 //                      group's lanes are adjacent in one wave and reduce their
 //                      absolute maximum with xor shuffles. HBM-bound.
-//   quant_group_regs   groups of up to 8192 elements that are a multiple of 8
-//                      (per-token rows): one workgroup per group held in
-//                      registers, block reduction, codes.
+//   quant_group_rowwave groups of up to 2048 elements that are a multiple of
+//                      8 (other than the powers of two above): one wave per
+//                      group held in registers, xor-shuffle reduction, codes.
+//   quant_group_regs   longer groups of up to 8192 elements (per-token rows):
+//                      one workgroup per group held in registers, block
+//                      reduction, codes. Both issue every load before the
+//                      first use.
 //   quant_group_block  any other group size (odd sizes, unaligned strides,
 //                      longer rows): one workgroup per group, block reduction,
 //                      then a second pass that re-reads the group (L2 hit).
@@ -40,29 +44,54 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTensorPartials = 512;
+// Groups that are multiples of 8 but not taken by the power-of-two kernel: up
+// to kRowWaveMaxGroup elements get one wave each, up to kThreads * 8 * 4 one
+// workgroup each. On bf16 [8192, 2048] one wave per row ran 1.6x faster than
+// one workgroup per row, on bf16 [8192, 4096] and [4096, 7168] 10-13 % slower.
+constexpr int64_t kRowWaveMaxGroup = 2048;
 
 // ---- element loads -----------------------------------------------------------
+// Eight consecutive elements as loaded (one 16-byte load for bf16/f16, two for
+// float32), converted to float32 on use: a 16-bit vector waiting in registers
+// takes 4 of them rather than 8.
 template <int XT>
-__device__ __forceinline__ void load8(const void* base, int64_t idx, float (&f)[8]) {
-  if constexpr (XT == Q8_F32) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
-    float4 a = p[0], b = p[1];
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-  } else {
-    const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+struct Vec8 {
+  uint4 w[XT == Q8_F32 ? 2 : 1];
+  __device__ __forceinline__ void load(const void* base, int64_t idx) {
+    if constexpr (XT == Q8_F32) {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + idx);
+      w[0] = p[0];
+      w[1] = p[1];
+    } else {
+      w[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    }
+  }
+  __device__ __forceinline__ void get(float (&f)[8]) const {
+    if constexpr (XT == Q8_F32) {
+      const uint32_t u[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (XT == Q8_BF16) {
-        f[2 * i] = __uint_as_float(w[i] << 16);
-        f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      } else {
-        f[2 * i] = f16_bits_to_f32(w[i] & 0xFFFFu);
-        f[2 * i + 1] = f16_bits_to_f32(w[i] >> 16);
+      for (int i = 0; i < 8; ++i) f[i] = __uint_as_float(u[i]);
+    } else {
+      const uint32_t u[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (XT == Q8_BF16) {
+          f[2 * i] = __uint_as_float(u[i] << 16);
+          f[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+        } else {
+          f[2 * i] = f16_bits_to_f32(u[i] & 0xFFFFu);
+          f[2 * i + 1] = f16_bits_to_f32(u[i] >> 16);
+        }
       }
     }
   }
+};
+
+template <int XT>
+__device__ __forceinline__ void load8(const void* base, int64_t idx, float (&f)[8]) {
+  Vec8<XT> v;
+  v.load(base, idx);
+  v.get(f);
 }
 
 template <int XT>
@@ -291,27 +320,34 @@ __global__ __launch_bounds__(kThreads) void quant_group_block(
 
 // One workgroup per group of up to kThreads * 8 * NV elements (a per-token
 // row, say) held in registers: one read of the input, a block reduction, then
-// the codes, instead of re-reading the group after the reduction.
+// the codes, instead of re-reading the group after the reduction. Each thread
+// owns NV slots of 8 consecutive elements and issues every slot's load before
+// the first use, so all of them are in flight together; a slot past the end
+// of the group re-reads the group's last 8 elements (repeats leave the maximum
+// unchanged) and stores nothing.
 template <int XT, bool FP8, int UE, int NV>
 __global__ __launch_bounds__(kThreads) void quant_group_regs(
     const void* __restrict__ x, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
-    float* __restrict__ s, int64_t g, float eps, float qmin, float qmax) {
+    float* __restrict__ s, uint32_t g, uint32_t groups_per_row, float eps, float qmin,
+    float qmax) {
   __shared__ float red[kThreads / kWave];
-  const int64_t groups_per_row = K / g;
-  const int64_t row = blockIdx.x / groups_per_row;
-  const int64_t j = blockIdx.x - row * groups_per_row;
-  const int64_t xb = row * ld_x + j * g;
-  const int64_t qb = row * K + j * g;
-  float f[NV][8];
+  const uint32_t row = blockIdx.x / groups_per_row;
+  const uint32_t j = blockIdx.x - row * groups_per_row;
+  const int64_t xb = (int64_t)row * ld_x + (int64_t)j * g;
+  const int64_t qb = (int64_t)row * K + (int64_t)j * g;
+  Vec8<XT> r[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const uint32_t i = (v * kThreads + threadIdx.x) * 8;
+    r[v].load(x, xb + (i < g ? i : g - 8));
+  }
   float a = 0.0f;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    const int64_t i = ((int64_t)v * kThreads + threadIdx.x) * 8;
-    if (i < g) {
-      load8<XT>(x, xb + i, f[v]);
+    float f[8];
+    r[v].get(f);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) a = fmaxf(a, fabsf(f[v][t]));
-    }
+    for (int t = 0; t < 8; ++t) a = fmaxf(a, fabsf(f[t]));
   }
   a = block_max(a, red);
   const float sc = group_scale<(UE != 0)>(a, eps, qmax);
@@ -319,10 +355,59 @@ __global__ __launch_bounds__(kThreads) void quant_group_regs(
   const Divider<(UE != 0)> div(sc);
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    const int64_t i = ((int64_t)v * kThreads + threadIdx.x) * 8;
+    const uint32_t i = (v * kThreads + threadIdx.x) * 8;
     if (i < g) {
-      float y[8];
-      div.apply8(f[v], y, qmin, qmax);
+      float f[8], y[8];
+      r[v].get(f);
+      div.apply8(f, y, qmin, qmax);
+      *reinterpret_cast<uint2*>(q + qb + i) = encode8<FP8>(y);
+    }
+  }
+}
+
+// One wave per group of up to kWave * 8 * NV elements, any multiple of 8 (not
+// only powers of two): lane l owns the 8-element slots l, l + 64, ... of the
+// group, loads all of them before the first use (a slot past the end re-reads
+// the group's last 8 elements and stores nothing), and the wave reduces the
+// maximum with xor shuffles: no LDS, no barrier. A workgroup holds kThreads /
+// kWave consecutive groups.
+template <int XT, bool FP8, int UE, int NV>
+__global__ __launch_bounds__(kThreads) void quant_group_rowwave(
+    const void* __restrict__ x, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
+    float* __restrict__ s, uint32_t ngroups, uint32_t g, uint32_t groups_per_row, float eps,
+    float qmin, float qmax) {
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t grp = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  if (grp >= ngroups) return;  // wave-uniform
+  const uint32_t row = grp / groups_per_row;
+  const uint32_t j = grp - row * groups_per_row;
+  const int64_t xb = (int64_t)row * ld_x + (int64_t)j * g;
+  const int64_t qb = (int64_t)row * K + (int64_t)j * g;
+  Vec8<XT> r[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const uint32_t i = (v * kWave + lane) * 8;
+    r[v].load(x, xb + (i < g ? i : g - 8));
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    float f[8];
+    r[v].get(f);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) a = fmaxf(a, fabsf(f[t]));
+  }
+  a = wave_max_xor(a, kWave);
+  const float sc = group_scale<(UE != 0)>(a, eps, qmax);
+  if (lane == 0) store_scale<UE>(s, grp, sc);
+  const Divider<(UE != 0)> div(sc);
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const uint32_t i = (v * kWave + lane) * 8;
+    if (i < g) {
+      float f[8], y[8];
+      r[v].get(f);
+      div.apply8(f, y, qmin, qmax);
       *reinterpret_cast<uint2*>(q + qb + i) = encode8<FP8>(y);
     }
   }
@@ -730,17 +815,31 @@ hipError_t dispatch(const QuantArgs& a, hipStream_t st) {
     const int64_t ngroups = a.M * (a.K / g);
     if (ngroups > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)ngroups);
+    const uint32_t g32 = (uint32_t)g, gpr = (uint32_t)(a.K / g);
+    if (vec && g % 8 == 0 && g <= kRowWaveMaxGroup) {
+      const int nv = (int)((g + kWave * 8 - 1) / (kWave * 8));
+      const dim3 wgrid((unsigned)((ngroups + kThreads / kWave - 1) / (kThreads / kWave)));
+#define Q8_ROWWAVE_CASE(NV)                                                                     \
+  case NV:                                                                                      \
+    hipLaunchKernelGGL((quant_group_rowwave<XT, FP8, UE, NV>), wgrid, blk, 0, st, a.x, a.K,     \
+                       a.ld_x, q, a.s, (uint32_t)ngroups, g32, gpr, a.eps, a.qmin, a.qmax);     \
+    break;
+      switch (nv <= 1 ? 1 : nv <= 2 ? 2 : 4) {
+        Q8_ROWWAVE_CASE(1) Q8_ROWWAVE_CASE(2) Q8_ROWWAVE_CASE(4)
+#undef Q8_ROWWAVE_CASE
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    }
     if (vec && g % 8 == 0 && g <= kThreads * 8 * 4) {
       const int nv = (int)((g + kThreads * 8 - 1) / (kThreads * 8));
-      if (nv == 1)
-        hipLaunchKernelGGL((quant_group_regs<XT, FP8, UE, 1>), grid, blk, 0, st, a.x, a.K, a.ld_x,
-                           q, a.s, g, a.eps, a.qmin, a.qmax);
-      else if (nv == 2)
-        hipLaunchKernelGGL((quant_group_regs<XT, FP8, UE, 2>), grid, blk, 0, st, a.x, a.K, a.ld_x,
-                           q, a.s, g, a.eps, a.qmin, a.qmax);
-      else
-        hipLaunchKernelGGL((quant_group_regs<XT, FP8, UE, 4>), grid, blk, 0, st, a.x, a.K, a.ld_x,
-                           q, a.s, g, a.eps, a.qmin, a.qmax);
+#define Q8_REGS_LAUNCH(NV)                                                                      \
+  hipLaunchKernelGGL((quant_group_regs<XT, FP8, UE, NV>), grid, blk, 0, st, a.x, a.K, a.ld_x,   \
+                     q, a.s, g32, gpr, a.eps, a.qmin, a.qmax)
+      if (nv == 1) Q8_REGS_LAUNCH(1);
+      else if (nv == 2) Q8_REGS_LAUNCH(2);
+      else Q8_REGS_LAUNCH(4);
+#undef Q8_REGS_LAUNCH
       return hipGetLastError();
     }
     if (vec && g % 8 == 0)

@@ -147,6 +147,43 @@ def test_per_token_rows_around_register_limit(K):
     check(x, K)
 
 
+@pytest.mark.parametrize("M,K,g,dtype,ue,int8", [
+    (130, 1536, 1536, "bf16", False, False),  # one wave per row, three slots a lane
+    (7, 2040, 2040, "f16", True, False),      # the last lanes re-read the row's end
+    (9, 3840, 1920, "f32", False, True),      # two groups per row, one wave each
+    (65, 2048, 2048, "bf16", False, True),    # per-token rows of 2048
+    (11, 7168, 3584, "bf16", True, False),    # two groups per row, one workgroup each
+    (257, 7168, 7168, "bf16", False, False),  # FP8 per-token rows of the prefill width
+    (5, 6000, 6000, "f32", False, True),      # f32 rows of one workgroup, ragged slots
+])
+def test_long_groups_wave_and_workgroup_kernels(M, K, g, dtype, ue, int8):
+    """Groups longer than 512 or not powers of two: one wave per group up to
+    2048 elements, one workgroup per group up to 8192."""
+    check(synth.activations(M, K, dtype, sigma=2.0, seed=M + g), g, ue, int8)
+
+
+@pytest.mark.parametrize("K,g", [(6144, 1536), (7168, 3584)])
+def test_e8m0_byte_scales_long_groups(K, g):
+    m = q8()
+    x = synth.activations(6, K, "bf16", seed=g)
+    q = torch.empty((6, K), dtype=torch.float8_e4m3fn, device=DEV)
+    s = torch.empty((6, K // g), dtype=torch.uint8, device=DEV)
+    m.quant_8bit(x.to(DEV), q, s, g, EPS, -448.0, 448.0, 2)
+    sync()
+    qo, so = oracle_quant(x, g, ue=True)
+    assert np.array_equal(s.cpu().numpy(), (so.view(np.uint32) >> 23).astype(np.uint8))
+    assert np.array_equal(codes(q).view(np.uint8), qo.view(np.uint8))
+
+
+@pytest.mark.parametrize("g", [1000, 3000])
+def test_strided_rows_long_groups(g):
+    full = synth.activations(20, 3016, "bf16", seed=g)
+    x = full[:, :3000]  # row stride 3016
+    qg, sg = run_quant(full.to(DEV)[:, :3000], g, int8=True)
+    qo, so = oracle_quant(x.contiguous(), g, int8=True)
+    assert np.array_equal(sg, so) and np.array_equal(qg.view(np.uint8), qo.view(np.uint8))
+
+
 @pytest.mark.parametrize("int8", [False, True])
 def test_per_tensor_dynamic(int8):
     m = q8()
