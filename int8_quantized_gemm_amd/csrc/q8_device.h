@@ -69,9 +69,31 @@ __device__ __forceinline__ f32x4 load_bias4(const void* b, int64_t n, int64_t n_
 }
 
 // ---- wave reductions ----------------------------------------------------------
+// Maximum of absolute values (floats >= +0, not NaN, whose bit patterns order
+// as unsigned integers) over aligned groups of `width` adjacent lanes (a power
+// of two, at most kWave), every lane of a group receiving it. Within a 16-lane
+// row each step is one DPP-modified integer max: quad_perm [1,0,3,2] and
+// [2,3,0,1] read lane ^ 1 and lane ^ 2; row_half_mirror reads lane 7 - i of
+// each 8-lane half row and row_mirror lane 15 - i of each row, which lie in the
+// partner group once the smaller groups hold their maxima. Wider steps permute
+// through LDS.
+template <int CTRL>
+__device__ __forceinline__ uint32_t umax_dpp(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+  return v > o ? v : o;
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int width) {
-  for (int off = width >> 1; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
+  uint32_t u = __float_as_uint(v);
+  if (width >= 2) u = umax_dpp<0xB1>(u);
+  if (width >= 4) u = umax_dpp<0x4E>(u);
+  if (width >= 8) u = umax_dpp<0x141>(u);
+  if (width >= 16) u = umax_dpp<0x140>(u);
+  for (int off = 16; off < width; off <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)u, off, kWave);
+    u = u > o ? u : o;
+  }
+  return __uint_as_float(u);
 }
 
 // Round a positive float32 up to a power of two (bitwise; powers of two unchanged).

@@ -182,12 +182,21 @@ __device__ __forceinline__ uint32_t encode_pair_bytes(float a, float b) {
   }
 }
 
+// Four codes in one dword, byte i from y[i]. FP8: the second convert writes
+// its pair into the high half of the first one's result.
+template <bool FP8>
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) {
+  if constexpr (FP8) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+  } else {
+    return encode_pair_bytes<false>(a, b) | (encode_pair_bytes<false>(c, d) << 16);
+  }
+}
+
 template <bool FP8>
 __device__ __forceinline__ uint2 encode8(const float (&y)[8]) {
-  uint2 r;
-  r.x = encode_pair_bytes<FP8>(y[0], y[1]) | (encode_pair_bytes<FP8>(y[2], y[3]) << 16);
-  r.y = encode_pair_bytes<FP8>(y[4], y[5]) | (encode_pair_bytes<FP8>(y[6], y[7]) << 16);
-  return r;
+  return uint2{encode4<FP8>(y[0], y[1], y[2], y[3]), encode4<FP8>(y[4], y[5], y[6], y[7])};
 }
 
 template <bool FP8>
@@ -641,13 +650,13 @@ __device__ __forceinline__ float silu_h(float g) {
   return g / d;  // IEEE division (correctly rounded)
 }
 
+// One range test selects the table or, rarely, the closed forms.
 __device__ __forceinline__ float silu_h_bf16(float g, const float* __restrict__ tab) {
   const uint32_t b = __float_as_uint(g) >> 16;  // the bf16 bits (g came from a bf16)
   const uint32_t e = (b >> 7) & 0xFFu;
-  const uint32_t ec = e < kSiluExpLo ? kSiluExpLo : (e >= kSiluExpHi ? kSiluExpHi - 1 : e);
-  const float t = tab[((b >> 15) << 12) | ((ec - kSiluExpLo) << 7) | (b & 127u)];
-  const float big = (b >> 15) ? -0.0f : g;
-  return e < kSiluExpLo ? g * 0.5f : (e >= kSiluExpHi ? big : t);
+  if (__builtin_expect(e - kSiluExpLo < kSiluExpHi - kSiluExpLo, 1))
+    return tab[((b >> 15) << 12) | ((e - kSiluExpLo) << 7) | (b & 127u)];
+  return e < kSiluExpLo ? g * 0.5f : ((b >> 15) ? -0.0f : g);
 }
 
 // Same work split as quant_fused_wave (16 outputs per lane, a group's TPG
@@ -675,7 +684,10 @@ __global__ __launch_bounds__(kSiluThreads) void quant_silu_bf16_table(
     const uint32_t row = vv / vpr;
     const bool live = v < total && row_live(masked_m, max_m, row);
     if (__ballot(live) == 0) continue;  // wave-uniform
+    // dead lanes take part in the shuffles with a = 0; y is read on live
+    // lanes only
     float y[2][8];
+    float a = 0.0f;
     if (live) {
       const int64_t off = (int64_t)row * ld_x + (int64_t)(vv - row * vpr) * 16;
       float u[2][8];
@@ -686,18 +698,11 @@ __global__ __launch_bounds__(kSiluThreads) void quant_silu_bf16_table(
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) y[h][i] = silu_h_bf16(y[h][i], tab) * u[h][i];
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) y[h][i] = 0.0f;
+        for (int i = 0; i < 8; ++i) {
+          y[h][i] = silu_h_bf16(y[h][i], tab) * u[h][i];
+          a = fmaxf(a, fabsf(y[h][i]));
+        }
     }
-    float a = 0.0f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(y[h][i]));
     a = wave_max_xor(a, TPG);
     if (!live) continue;
     const float sc = group_scale<(UE != 0)>(a, eps, qmax);
