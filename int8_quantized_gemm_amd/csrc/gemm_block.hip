@@ -975,20 +975,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_stream_pk(TileParams p) {
 // Streaming (decode) kernel with shared activations: M <= 16, K a multiple of 1024
 // ------------------------------------------------------------------------------
 
-// The part of such a fragment that belongs to 32-wide K block s of the chunk:
-// the half s>>1 of the lane groups with g>>1 == s&1; everything else zeroed.
-__device__ __forceinline__ i32x8 block32_part(const i32x8& f, int s, int g) {
-  const bool mine = (g >> 1) == (s & 1);
-  const bool hi = (s >> 1) != 0;
-  i32x8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = (mine && !hi) ? f[i] : 0;
-    r[4 + i] = (mine && hi) ? f[4 + i] : 0;
-  }
-  return r;
-}
-
 // Every workgroup needs all M activation rows and their scales. Read from L2
 // by every wave, those few lines are requested by thousands of waves at once
 // and serialise on their L2 channels; here one linear pass per workgroup
@@ -1071,8 +1057,7 @@ void gemm_stream_sa(TileParams p) {
 #pragma unroll
     for (int s = 0; s < KSUB; ++s) {
       const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsl), u * KSUB + s));
-      const i32x8 a = KS == 128 ? af : block32_part(af, s, g);
-      const f32x4 pr = mfma_fp8_k128(wf[u], a);
+      const f32x4 pr = KS == 128 ? mfma_fp8_k128(wf[u], af) : mfma_block(wf[u], af, block_selector(g, s));
       acc = fma4s(pr, sa[s] * ws, acc);
     }
   }
