@@ -23,9 +23,11 @@
 // four outputs share one activation row and one scale product), and sum the
 // waves' float32 partials in a fixed order through LDS (deterministic):
 // gemm_stream     one workgroup per 16 W rows, waves splitting the K chunks;
-// gemm_stream_pk  up to 8 rows, 32-wide blocks: four rows' block partials per
-//                 MFMA (column j of the activation operand is one row's block);
-// gemm_stream_sa  8..16 rows: the activation rows staged in LDS per workgroup;
+// gemm_stream_pk  up to 4 rows (8 where the staged kernel does not fit),
+//                 32-wide blocks: four rows' block partials per MFMA (column j
+//                 of the activation operand is one row's block);
+// gemm_stream_sa  5..16 rows with 32-wide blocks, 8..16 with 128-wide: the
+//                 activation rows staged in LDS per workgroup;
 // gemm_split_mid  17..64 rows: K split into ranges, 64 W rows per workgroup,
 //                 the range's activation slice in LDS, float32 partials in the
 //                 caller's workspace, summed in order by gemm_split_reduce;
@@ -1541,13 +1543,17 @@ hipError_t launch_blockwise(const BlockGemmArgs& a, hipStream_t st) {
     if (mid_plan(a.M, a.N, a.K, a.bk, pl) && a.workspace && (uintptr_t)a.workspace % 16 == 0 &&
         (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.As % 16 == 0)
       return launch_mid(tp, pl, a.bk, static_cast<float*>(a.workspace), st);
-    // from 8 activation rows on, staging them once per workgroup beats every
-    // wave reading them from L2 (measured: M = 16 12.2 -> 10.8 us, M = 1 and
-    // 4 slightly slower staged)
-    if (a.M >= 8 && stream_sa_fits(a.M, a.K, tp.KB) && (uintptr_t)a.A % 16 == 0 &&
+    // staging the activation rows once per workgroup beats every wave reading
+    // them from L2 from 8 rows on (measured: M = 16 12.2 -> 10.8 us, M = 1 and
+    // 4 slightly slower staged), and with 32-wide blocks beats the packed
+    // kernel below from 5 rows on (M = 5 / 6 / 7 / 8: 9.44 / 9.46 / 9.51 /
+    // 9.56 us packed, 9.14 / 9.21 / 9.14 / 9.12 us staged)
+    const int64_t sa_min = a.bk == 32 ? 5 : 8;
+    if (a.M >= sa_min && stream_sa_fits(a.M, a.K, tp.KB) && (uintptr_t)a.A % 16 == 0 &&
         (uintptr_t)a.As % 16 == 0)
       return a.bk == 128 ? launch_stream_sa<128>(tp, st) : launch_stream_sa<32>(tp, st);
-    // up to 8 rows and 32-wide blocks: four rows' block partials per MFMA
+    // 32-wide blocks, up to 8 rows (4 when the staged kernel fits): four rows'
+    // block partials per MFMA
     if (a.bk == 32 && a.M <= 8) return launch_stream_pk(tp, st);
     return a.bk == 128 ? launch_stream<128>(tp, st) : launch_stream<32>(tp, st);
   }

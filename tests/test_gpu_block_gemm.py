@@ -68,13 +68,22 @@ def test_decode_block32_ue8m0(M):
 
 
 @pytest.mark.parametrize("M,N,K", [(8, 1000, 1024), (13, 520, 2048), (16, 4096, 8192),
-                                   (9, 48, 3072), (16, 16, 1024)])
+                                   (9, 48, 3072), (16, 16, 1024), (5, 1000, 1024),
+                                   (7, 4096, 7168)])
 @pytest.mark.parametrize("bk", [128, 32])
 def test_decode_shared_activation_shapes(M, N, K, bk):
-    """8..16 activation rows with K a multiple of 1024 take the kernel that
-    stages the activations once per workgroup: waves without K chunks
-    (K = 1024), ragged N, the largest K it accepts (8192)."""
+    """8..16 activation rows (5..16 with 32-wide blocks) with K a multiple of
+    1024 take the kernel that stages the activations once per workgroup:
+    waves without K chunks (K = 1024), ragged N, the largest K it accepts
+    (8192); 5 and 7 rows with 128-wide blocks take the plain streaming kernel."""
     run_case(M, N, K, bk, bk, ue=(bk == 32), bias=True, seed=M * 7 + K)
+
+
+@pytest.mark.parametrize("M", [5, 6, 8])
+def test_decode_packed_two_row_groups(M):
+    """5..8 rows, 32-wide blocks, K not a multiple of 1024: the packed kernel
+    with two four-row MFMA groups (the staged kernel does not apply)."""
+    run_case(M, 520, 1536, 32, 32, ue=True, bias=True, seed=M)
 
 
 @pytest.mark.parametrize("M,N,K,bn,bk", [(17, 1000, 1024, 128, 128), (33, 4096, 7168, 32, 32),
