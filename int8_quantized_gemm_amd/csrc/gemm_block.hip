@@ -23,10 +23,10 @@
 // four outputs share one activation row and one scale product), and sum the
 // waves' float32 partials in a fixed order through LDS (deterministic):
 // gemm_stream     one workgroup per 16 W rows, waves splitting the K chunks;
-// gemm_stream_pk  up to 4 rows (8 where the staged kernel does not fit),
+// gemm_stream_pk  up to 2 rows (8 where the staged kernel does not fit),
 //                 32-wide blocks: four rows' block partials per MFMA (column j
 //                 of the activation operand is one row's block);
-// gemm_stream_sa  5..16 rows with 32-wide blocks, 8..16 with 128-wide: the
+// gemm_stream_sa  3..16 rows with 32-wide blocks, 8..16 with 128-wide: the
 //                 activation rows staged in LDS per workgroup;
 // gemm_split_mid  17..64 rows: K split into ranges, 64 W rows per workgroup,
 //                 the range's activation slice in LDS, float32 partials in the
@@ -1327,18 +1327,22 @@ hipError_t launch_stream_mt(const TileParams& tp, hipStream_t st) {
 }
 
 constexpr int64_t kLdsBytes = 160 * 1024;
-constexpr int kStreamSaNW = 16;
-constexpr int kStreamSaR = 4;
+// gemm_stream_sa: eight waves, each with all of its chunks' loads in flight
+// (against sixteen waves of up to four chunks, one process, launches
+// interleaved, 32-wide blocks, N = 4096, K = 7168: M = 5 / 8 / 12 / 16
+// 9.09 / 9.15 / 9.75 / 10.26 -> 8.21 / 8.52 / 8.93 / 9.40 us)
+constexpr int kStreamSaNW = 8;
+constexpr int kStreamSaMaxR = 8;
 
 // dynamic LDS of gemm_stream_sa
 inline int64_t stream_sa_lds(int64_t M, int64_t K, int KB) {
   return M * (K + 16) + ((M * KB * 4 + 1023) & ~1023LL) + (int64_t)kStreamSaNW * 64 * 16;
 }
 
-// M <= 16, K a multiple of 1024, at most kStreamSaR chunks of 128 per wave,
+// M <= 16, K a multiple of 1024, at most kStreamSaMaxR chunks of 128 per wave,
 // and the staged activations fit in LDS
 inline bool stream_sa_fits(int64_t M, int64_t K, int KB) {
-  return M <= 16 && K % 1024 == 0 && (K / 128 + kStreamSaNW - 1) / kStreamSaNW <= kStreamSaR &&
+  return M <= 16 && K % 1024 == 0 && (K / 128 + kStreamSaNW - 1) / kStreamSaNW <= kStreamSaMaxR &&
          stream_sa_lds(M, K, KB) <= kLdsBytes;
 }
 
@@ -1357,9 +1361,9 @@ hipError_t raise_lds_limit(const void* kern, std::atomic<uint64_t>& done) {
   return e;
 }
 
-template <int KS>
-hipError_t launch_stream_sa(const TileParams& tp, hipStream_t st) {
-  const auto kern = gemm_stream_sa<KS, kStreamSaNW, kStreamSaR>;
+template <int KS, int R>
+hipError_t launch_stream_sa_r(const TileParams& tp, hipStream_t st) {
+  const auto kern = gemm_stream_sa<KS, kStreamSaNW, R>;
   static std::atomic<uint64_t> lds_raised{0};
   const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kern), lds_raised);
   if (e != hipSuccess) return e;
@@ -1367,6 +1371,16 @@ hipError_t launch_stream_sa(const TileParams& tp, hipStream_t st) {
   const unsigned lds = (unsigned)stream_sa_lds(tp.M, tp.K, tp.KB);
   hipLaunchKernelGGL(kern, dim3((unsigned)((tp.N + 15) / 16)), dim3(kStreamSaNW * 64), lds, st, tp);
   return hipGetLastError();
+}
+
+// R: the fewest of 2, 4, 7 or 8 chunks per wave that covers K
+template <int KS>
+hipError_t launch_stream_sa(const TileParams& tp, hipStream_t st) {
+  const int64_t per = (tp.K / 128 + kStreamSaNW - 1) / kStreamSaNW;
+  if (per <= 2) return launch_stream_sa_r<KS, 2>(tp, st);
+  if (per <= 4) return launch_stream_sa_r<KS, 4>(tp, st);
+  if (per <= 7) return launch_stream_sa_r<KS, 7>(tp, st);
+  return launch_stream_sa_r<KS, 8>(tp, st);
 }
 
 template <int MT4>
@@ -1546,13 +1560,13 @@ hipError_t launch_blockwise(const BlockGemmArgs& a, hipStream_t st) {
     // staging the activation rows once per workgroup beats every wave reading
     // them from L2 from 8 rows on (measured: M = 16 12.2 -> 10.8 us, M = 1 and
     // 4 slightly slower staged), and with 32-wide blocks beats the packed
-    // kernel below from 5 rows on (M = 5 / 6 / 7 / 8: 9.44 / 9.46 / 9.51 /
-    // 9.56 us packed, 9.14 / 9.21 / 9.14 / 9.12 us staged)
-    const int64_t sa_min = a.bk == 32 ? 5 : 8;
+    // kernel below from 3 rows on (M = 1 / 2 / 3 / 4: 7.92 / 7.97 / 8.15 /
+    // 8.21 us packed, 8.01 / 7.95 / 7.90 / 8.01 us staged)
+    const int64_t sa_min = a.bk == 32 ? 3 : 8;
     if (a.M >= sa_min && stream_sa_fits(a.M, a.K, tp.KB) && (uintptr_t)a.A % 16 == 0 &&
         (uintptr_t)a.As % 16 == 0)
       return a.bk == 128 ? launch_stream_sa<128>(tp, st) : launch_stream_sa<32>(tp, st);
-    // 32-wide blocks, up to 8 rows (4 when the staged kernel fits): four rows'
+    // 32-wide blocks, up to 8 rows (2 when the staged kernel fits): four rows'
     // block partials per MFMA
     if (a.bk == 32 && a.M <= 8) return launch_stream_pk(tp, st);
     return a.bk == 128 ? launch_stream<128>(tp, st) : launch_stream<32>(tp, st);

@@ -340,7 +340,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_stream_mx(MxParams p) {
 }
 
 // ---- up to 16 rows: activations staged in LDS once per workgroup ---------------
-constexpr int kMxSaNW = 16, kMxSaR = 4;
+// eight waves, each with all of its chunks' loads in flight (against sixteen
+// waves of up to four chunks, N = 4096, K = 7168: M = 1 / 4 / 8 / 16
+// 7.64 / 7.88 / 8.18 / 8.98 -> 7.46 / 7.64 / 7.87 / 8.62 us)
+constexpr int kMxSaNW = 8, kMxSaMaxR = 8;
 
 // dynamic LDS: activation rows (pitch K + 16), scale bytes rounded up to whole
 // 1 KB copies, and the waves' partials
@@ -349,7 +352,7 @@ inline int64_t stream_mx_sa_lds(int64_t M, int64_t K) {
 }
 
 inline bool stream_mx_sa_fits(int64_t M, int64_t K) {
-  return M >= 1 && M <= 16 && K % 1024 == 0 && (K / 128 + kMxSaNW - 1) / kMxSaNW <= kMxSaR &&
+  return M >= 1 && M <= 16 && K % 1024 == 0 && (K / 128 + kMxSaNW - 1) / kMxSaNW <= kMxSaMaxR &&
          stream_mx_sa_lds(M, K) <= 160 * 1024;
 }
 
@@ -656,8 +659,9 @@ hipError_t launch_split_mx_inst(const MxParams& p, const MxMidPlan& pl, float* p
   return hipGetLastError();
 }
 
-hipError_t launch_stream_mx_sa(const MxParams& p, hipStream_t st) {
-  const auto kern = gemm_stream_mx_sa<kMxSaNW, kMxSaR>;
+template <int R>
+hipError_t launch_stream_mx_sa_r(const MxParams& p, hipStream_t st) {
+  const auto kern = gemm_stream_mx_sa<kMxSaNW, R>;
   static std::atomic<uint64_t> lds_raised{0};
   const hipError_t e = raise_lds_limit_mx(reinterpret_cast<const void*>(kern), lds_raised);
   if (e != hipSuccess) return e;
@@ -665,6 +669,15 @@ hipError_t launch_stream_mx_sa(const MxParams& p, hipStream_t st) {
   hipLaunchKernelGGL(kern, dim3((unsigned)((p.N + 15) / 16)), dim3(kMxSaNW * 64),
                      (unsigned)stream_mx_sa_lds(p.M, p.K), st, p);
   return hipGetLastError();
+}
+
+// R: the fewest of 2, 4, 7 or 8 chunks per wave that covers K
+hipError_t launch_stream_mx_sa(const MxParams& p, hipStream_t st) {
+  const int64_t per = (p.K / 128 + kMxSaNW - 1) / kMxSaNW;
+  if (per <= 2) return launch_stream_mx_sa_r<2>(p, st);
+  if (per <= 4) return launch_stream_mx_sa_r<4>(p, st);
+  if (per <= 7) return launch_stream_mx_sa_r<7>(p, st);
+  return launch_stream_mx_sa_r<8>(p, st);
 }
 
 template <int MT>

@@ -62,7 +62,7 @@ def test_tiny_fp32_block128():
     run_case(4, 256, 512, 128, 128, x_dtype="f32")
 
 
-@pytest.mark.parametrize("M", [1, 4, 8, 12, 16, 64])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 12, 16, 64])
 def test_decode_block32_ue8m0(M):
     run_case(M, 4096, 7168, 32, 32, ue=True, outliers=0.01)
 
