@@ -26,7 +26,7 @@
 // gemm_stream_pk  up to 2 rows (8 where the staged kernel does not fit),
 //                 32-wide blocks: four rows' block partials per MFMA (column j
 //                 of the activation operand is one row's block);
-// gemm_stream_sa  3..16 rows with 32-wide blocks, 8..16 with 128-wide: the
+// gemm_stream_sa  3..16 rows with 32-wide blocks, 1..16 with 128-wide: the
 //                 activation rows staged in LDS per workgroup;
 // gemm_split_mid  17..64 rows: K split into ranges, 64 W rows per workgroup,
 //                 the range's activation slice in LDS, float32 partials in the
@@ -1558,11 +1558,12 @@ hipError_t launch_blockwise(const BlockGemmArgs& a, hipStream_t st) {
         (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.As % 16 == 0)
       return launch_mid(tp, pl, a.bk, static_cast<float*>(a.workspace), st);
     // staging the activation rows once per workgroup beats every wave reading
-    // them from L2 from 8 rows on (measured: M = 16 12.2 -> 10.8 us, M = 1 and
-    // 4 slightly slower staged), and with 32-wide blocks beats the packed
-    // kernel below from 3 rows on (M = 1 / 2 / 3 / 4: 7.92 / 7.97 / 8.15 /
-    // 8.21 us packed, 8.01 / 7.95 / 7.90 / 8.01 us staged)
-    const int64_t sa_min = a.bk == 32 ? 3 : 8;
+    // them from L2 at any row count with 128-wide blocks (N = 4096, K = 7168,
+    // M = 1 / 2 / 4 / 7: 8.03 / 8.69 / 8.99 / 9.74 us unstaged, 7.28 / 7.35 /
+    // 7.55 / 7.76 us staged), and with 32-wide blocks beats the packed kernel
+    // below from 3 rows on (M = 1 / 2 / 3 / 4: 7.92 / 7.97 / 8.15 / 8.21 us
+    // packed, 8.01 / 7.95 / 7.90 / 8.01 us staged)
+    const int64_t sa_min = a.bk == 32 ? 3 : 1;
     if (a.M >= sa_min && stream_sa_fits(a.M, a.K, tp.KB) && (uintptr_t)a.A % 16 == 0 &&
         (uintptr_t)a.As % 16 == 0)
       return a.bk == 128 ? launch_stream_sa<128>(tp, st) : launch_stream_sa<32>(tp, st);

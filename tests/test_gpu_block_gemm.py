@@ -69,14 +69,21 @@ def test_decode_block32_ue8m0(M):
 
 @pytest.mark.parametrize("M,N,K", [(8, 1000, 1024), (13, 520, 2048), (16, 4096, 8192),
                                    (9, 48, 3072), (16, 16, 1024), (5, 1000, 1024),
-                                   (7, 4096, 7168)])
+                                   (7, 4096, 7168), (1, 4096, 7168), (3, 520, 3072)])
 @pytest.mark.parametrize("bk", [128, 32])
 def test_decode_shared_activation_shapes(M, N, K, bk):
-    """8..16 activation rows (5..16 with 32-wide blocks) with K a multiple of
-    1024 take the kernel that stages the activations once per workgroup:
-    waves without K chunks (K = 1024), ragged N, the largest K it accepts
-    (8192); 5 and 7 rows with 128-wide blocks take the plain streaming kernel."""
+    """Up to 16 activation rows with 128-wide blocks (3..16 with 32-wide) and
+    K a multiple of 1024 take the kernel that stages the activations once per
+    workgroup: waves without K chunks (K = 1024), one, two, four, seven or
+    eight chunks per wave, ragged N, the largest K it accepts (8192)."""
     run_case(M, N, K, bk, bk, ue=(bk == 32), bias=True, seed=M * 7 + K)
+
+
+@pytest.mark.parametrize("M,K", [(1, 1536), (3, 2560), (16, 1536)])
+def test_decode_unstaged_128_blocks(M, K):
+    """128-wide blocks with K not a multiple of 1024: the streaming kernel
+    whose waves read the activations from L2."""
+    run_case(M, 520, K, 128, 128, bias=True, seed=M + K)
 
 
 @pytest.mark.parametrize("M", [5, 6, 8])
