@@ -977,6 +977,25 @@ __global__ __launch_bounds__(NW * 64) void gemm_stream_pk(TileParams p) {
 // Streaming (decode) kernel with shared activations: M <= 16, K a multiple of 1024
 // ------------------------------------------------------------------------------
 
+// Activation rows and their scales -> LDS, the rows at a pitch of a_pitch
+// bytes (rows are K bytes, K a multiple of 1024, so no 1 KB load crosses a
+// row); the scale copy is rounded up to whole 1 KB loads, the tail reading
+// zeros from the resource's range check. Wave w of NW issues every NW-th load.
+template <int NW>
+__device__ __forceinline__ void stage_rows(const TileParams& p, uint32_t a_pitch, uint32_t s_bytes,
+                                           uint8_t* sA, uint8_t* sS, int w, int lane) {
+  const int64_t M = p.M, K = p.K;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (uint32_t)(M * K));
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(p.As, s_bytes);
+  const int per_row = (int)(K / 1024), a_loads = (int)M * per_row;
+  for (int i = w; i < a_loads; i += NW) {
+    const int row = i / per_row, col = (i - row * per_row) * 1024;
+    b2l16(rA, (uint32_t)lane * 16, (uint32_t)i * 1024, sA + row * a_pitch + col);
+  }
+  const int s_loads = (int)((s_bytes + 1023u) >> 10);
+  for (int i = w; i < s_loads; i += NW) b2l16(rS, (uint32_t)lane * 16, (uint32_t)i * 1024, sS + i * 1024);
+}
+
 // Every workgroup needs all M activation rows and their scales. Read from L2
 // by every wave, those few lines are requested by thousands of waves at once
 // and serialise on their L2 channels; here one linear pass per workgroup
@@ -1006,20 +1025,7 @@ void gemm_stream_sa(TileParams p) {
   uint8_t* sS = smem + M * a_pitch;
   f32x4* red = reinterpret_cast<f32x4*>(sS + ((s_bytes + 1023u) & ~1023u));  // [NW][64]
 
-  // ---- activations and scales -> LDS (rows are K bytes, K a multiple of
-  // 1024, so no load crosses a row); the scale copy is rounded up to whole
-  // 1 KB loads, the tail reading zeros from the resource's range check
-  {
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (uint32_t)(M * K));
-    const __amdgpu_buffer_rsrc_t rS = make_rsrc(p.As, s_bytes);
-    const int per_row = (int)(K / 1024), a_loads = (int)M * per_row;
-    for (int i = w; i < a_loads; i += NW) {
-      const int row = i / per_row, col = (i - row * per_row) * 1024;
-      b2l16(rA, (uint32_t)lane * 16, (uint32_t)i * 1024, sA + row * a_pitch + col);
-    }
-    const int s_loads = (int)((s_bytes + 1023u) >> 10);
-    for (int i = w; i < s_loads; i += NW) b2l16(rS, (uint32_t)lane * 16, (uint32_t)i * 1024, sS + i * 1024);
-  }
+  stage_rows<NW>(p, a_pitch, s_bytes, sA, sS, w, lane);
   // this wave's weight scales (one per lane) and weight chunks, issued after
   // the LDS copies so that waiting for the copies leaves them in flight
   const float* wsp = p.Ws + (n0 / p.bn) * KB;  // n0, bn multiples of 16: one block
