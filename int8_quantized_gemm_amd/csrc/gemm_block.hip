@@ -1443,7 +1443,10 @@ inline bool mid_plan(int64_t M, int64_t N, int64_t K, int bk, MidPlan& pl) {
   pl.Kc = (int)(K / best);
   const int ncc = pl.Kc / 128;
   const int need = (ncc + kMidNW / 4 - 1) / (kMidNW / 4);
-  pl.R = need <= 4 ? 4 : 8;
+  // chunks per wave rounded up to 4, 7 or 8 (a clamped duplicate load for
+  // each chunk short: M = 24 / 48 / 64 at K = 7168, 7 chunks, 13.98 / 16.19 /
+  // 18.60 us with R = 8, 13.45 / 15.77 / 17.84 us with R = 7)
+  pl.R = need <= 4 ? 4 : (need <= 7 ? 7 : 8);
   pl.mt = (int)((M + 15) / 16);
   const int64_t kbc = pl.Kc / bk;
   const int64_t a_bytes = ((M * pl.Kc) + 1023) & ~1023LL;
@@ -1472,7 +1475,8 @@ hipError_t launch_mid_inst(const TileParams& tp, const MidPlan& pl, float* part,
 template <int KS, int MT>
 hipError_t launch_mid_r(const TileParams& tp, const MidPlan& pl, float* part, hipStream_t st) {
   return pl.R == 4 ? launch_mid_inst<KS, MT, 4>(tp, pl, part, st)
-                   : launch_mid_inst<KS, MT, 8>(tp, pl, part, st);
+         : pl.R == 7 ? launch_mid_inst<KS, MT, 7>(tp, pl, part, st)
+                     : launch_mid_inst<KS, MT, 8>(tp, pl, part, st);
 }
 
 template <int KS>

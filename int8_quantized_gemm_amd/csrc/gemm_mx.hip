@@ -621,7 +621,11 @@ bool mx_mid_plan(int64_t M, int64_t N, int64_t K, MxMidPlan& pl) {
   pl.S = best;
   pl.Kc = (int)(K / best);
   const int ncc = pl.Kc / 128;
-  pl.R = (ncc + 1) / 2 <= 4 ? 4 : 8;
+  // chunks per wave rounded up to 4, 7 or 8 (as for the float32-scale split;
+  // M = 24 / 48 / 64 at K = 7168: 11.79 / 13.00 / 14.32 us with R = 8,
+  // 11.41 / 12.67 / 14.05 us with R = 7)
+  const int need = (ncc + 1) / 2;
+  pl.R = need <= 4 ? 4 : (need <= 7 ? 7 : 8);
   pl.mt = (int)((M + 15) / 16);
   const int64_t a_bytes = ((M * pl.Kc) + 1023) & ~1023LL;
   const int64_t s_bytes = ((M * ncc + 63) / 64) * 64 * 4;
@@ -682,7 +686,9 @@ hipError_t launch_stream_mx_sa(const MxParams& p, hipStream_t st) {
 
 template <int MT>
 hipError_t launch_split_mx_r(const MxParams& p, const MxMidPlan& pl, float* part, hipStream_t st) {
-  return pl.R == 4 ? launch_split_mx_inst<MT, 4>(p, pl, part, st) : launch_split_mx_inst<MT, 8>(p, pl, part, st);
+  return pl.R == 4   ? launch_split_mx_inst<MT, 4>(p, pl, part, st)
+         : pl.R == 7 ? launch_split_mx_inst<MT, 7>(p, pl, part, st)
+                     : launch_split_mx_inst<MT, 8>(p, pl, part, st);
 }
 
 hipError_t launch_split_mx(const MxParams& p, const MxMidPlan& pl, float* part, hipStream_t st) {
