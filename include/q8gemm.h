@@ -9,10 +9,11 @@
  *   allocates every buffer, outputs and workspace included; outputs are
  *   written in place. The library never allocates or frees memory and may be
  *   called from several threads at once. Its process-wide state: per-device
- *   records that a kernel's LDS limit was raised, and, for the one
- *   allocation-free entry point (moe_mm_data_noalloc), a fixed device array
- *   per GPU and its device address, looked up once per device; each is set
- *   once and thread-safe.
+ *   records that a kernel's LDS limit was raised and of the compute-unit
+ *   count, for the one allocation-free entry point (moe_mm_data_noalloc) a
+ *   fixed device array per GPU and its device address, looked up once per
+ *   device; a call counter (blockwise_scaled_mm tokens) and the setting of
+ *   q8gemm_set_split_wait_us. All of it is thread-safe.
  * - Every matrix is row-major and contiguous unless a leading dimension is
  *   passed. Weights are [N, K] with K contiguous (the "nt" layout: a
  *   column-major [K, N] weight is the same bytes).
@@ -62,6 +63,17 @@ typedef enum {
 
 /* Message describing the last failed call on this thread ("" if none). */
 const char* q8gemm_last_error(void);
+
+/*
+ * Longest time the first part of a split tile (blockwise_scaled_mm with
+ * more than 64 rows and a workspace) waits for its second part, in
+ * microseconds, for later calls of this process: default 200, at most
+ * 100000. A first part whose second part is not done by then (its
+ * workgroup did not get a compute unit in time) computes the rest of K
+ * itself. 0: first parts never wait, so every tile's outputs equal the
+ * unsplit kernel's bit for bit (testing). Q8_EINVAL outside [0, 100000].
+ */
+int q8gemm_set_split_wait_us(int microseconds);
 
 /*
  * 8-bit activation quantization.
@@ -139,11 +151,26 @@ int quant_8bit(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, int64_t ld
  * A, W and As each below 4 GiB (Q8_EUNSUPPORTED otherwise).
  * Accumulation: FP8 products summed in float32 per K block, scaled and
  * summed in float32.
- * workspace: blockwise_scaled_mm_workspace_size() bytes, 16-byte aligned:
- * float32 split-K partials for decode batches of 17..64 rows (S x M x N
- * floats, S the number of K ranges; 4 MiB for 64 x 4096 x 7168), 0 for every
- * other shape (then NULL is allowed). Q8_EWORKSPACE if it is needed and
- * missing or short. The contents need no initialisation and are overwritten.
+ * workspace: blockwise_scaled_mm_workspace_size() bytes, 16-byte aligned.
+ * - 17..64 rows: float32 split-K partials (S x M x N floats, S the number of
+ *   K ranges; 4 MiB for 64 x 4096 x 7168); required (Q8_EWORKSPACE if
+ *   missing or short).
+ * - more than 64 rows, K a multiple of 128 and at least 1024: optional. The
+ *   LDS-tiled kernel runs one 256 x 256 tile per compute unit at a time; when
+ *   the tile count T leaves a last round of R = T mod C tiles on the device's
+ *   C compute units with 0 < R <= C / 2, those R tiles are each split in K
+ *   between two workgroups (idle units run the second parts), which needs R
+ *   float32 tile partials and R flag words (32 MiB for 4096 x 18432 on 256
+ *   units; 4096 x 7168, R = 192, is not split). Without a workspace of that
+ *   size every tile runs whole. A
+ *   split tile adds two float32 partial sums, so its outputs can differ from
+ *   the unsplit ones in the last bits; each way is deterministic (a tile's
+ *   first part comes out as unsplit when its second part is late, see
+ *   q8gemm_set_split_wait_us). The size depends on the current device.
+ * - 0 for every other shape (then NULL is allowed).
+ * The contents need no initialisation (flag words hold any value between
+ * calls) and are overwritten. Calls that may overlap in time (other streams)
+ * must not share a workspace.
  */
 size_t blockwise_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K, int bn, int bk);
 int blockwise_scaled_mm(const void* A, const float* As, const void* W, const float* Ws,

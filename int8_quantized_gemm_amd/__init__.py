@@ -37,7 +37,7 @@ Q8_F32, Q8_BF16, Q8_F16, Q8_E4M3FN, Q8_I8, Q8_I32 = 0, 1, 2, 3, 4, 5
 SCALE_PER_GROUP, SCALE_PER_TENSOR_DYNAMIC, SCALE_STATIC = 0, 1, 2
 
 EXPORTS = (
-    "q8gemm_last_error",
+    "q8gemm_last_error", "q8gemm_set_split_wait_us",
     "quant_8bit_workspace_size", "quant_8bit",
     "blockwise_scaled_mm_workspace_size", "blockwise_scaled_mm",
     "blockwise_scaled_mm_e8m0_workspace_size", "blockwise_scaled_mm_e8m0",
@@ -60,6 +60,7 @@ def _sig(name, res, *args):
 
 
 _lib_last_error = _sig("q8gemm_last_error", ctypes.c_char_p)
+_split_wait = _sig("q8gemm_set_split_wait_us", _i, _i)
 _quant_ws = _sig("quant_8bit_workspace_size", _sz, _i64, _i64, _i)
 _quant = _sig("quant_8bit", _i, _p, _i, _i64, _i64, _i64, _p, _i, _p, _i64, _i, _f, _f, _f, _i, _i,
               _p, _i64, _p, _sz, _p)
@@ -96,6 +97,12 @@ def last_error() -> str:
 def _check(status: int) -> None:
     if status != Q8_OK:
         raise Q8Error(status, last_error())
+
+
+def set_split_wait_us(microseconds: int) -> None:
+    """Longest wait of a split tile's first part for its second part (see
+    ``blockwise_scaled_mm``); 0 makes every tile come out as unsplit."""
+    _check(_split_wait(int(microseconds)))
 
 
 _DT = {

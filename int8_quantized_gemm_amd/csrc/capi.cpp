@@ -56,6 +56,13 @@ extern "C" {
 
 const char* q8gemm_last_error(void) { return g_last_error.c_str(); }
 
+int q8gemm_set_split_wait_us(int microseconds) {
+  if (microseconds < 0 || microseconds > 100000)
+    return fail(Q8_EINVAL, "q8gemm_set_split_wait_us: %d outside [0, 100000]", microseconds);
+  q8::set_split_wait_ticks((uint32_t)microseconds * 100u);
+  return ok();
+}
+
 size_t quant_8bit_workspace_size(int64_t M, int64_t K, q8_scale_mode mode) {
   if (mode != Q8_SCALE_PER_TENSOR_DYNAMIC) return 0;
   return q8::quant_partials_count(M, K) * sizeof(float);
@@ -118,7 +125,7 @@ int quant_8bit(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, int64_t ld
 size_t blockwise_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K, int bn, int bk) {
   if (M < 0 || N < 1 || K < 1 || (bk != 32 && bk != 128) || bn < 16 || bn % 16 != 0 || K % bk != 0)
     return 0;
-  return q8::blockwise_workspace_bytes(M, N, K, bn, bk);
+  return q8::blockwise_workspace_bytes(M, N, K, bn, bk) + q8::blockwise_split_bytes(M, N, K, bn, bk);
 }
 
 int blockwise_scaled_mm(const void* A, const float* As, const void* W, const float* Ws,
@@ -131,17 +138,22 @@ int blockwise_scaled_mm(const void* A, const float* As, const void* W, const flo
   if (r != Q8_OK) return r;
   if (M == 0) return ok();
   if (!A || !As || !W || !Ws || !D) return fail(Q8_EINVAL, "%s: null pointer", fn);
-  const size_t need = blockwise_scaled_mm_workspace_size(M, N, K, bn, bk);
+  // the decode split needs its workspace; the split of a last round of tiles
+  // (M > 64) uses one when it is given and large enough
+  const size_t need = q8::blockwise_workspace_bytes(M, N, K, bn, bk);
+  const size_t want = need ? 0 : q8::blockwise_split_bytes(M, N, K, bn, bk);
   if (need && (!workspace || workspace_bytes < need))
     return fail(Q8_EWORKSPACE, "%s: workspace needs %zu bytes", fn, need);
-  if (need && (uintptr_t)workspace % 16 != 0)
+  const bool use_ws = need || (want && workspace && workspace_bytes >= want);
+  if (use_ws && (uintptr_t)workspace % 16 != 0)
     return fail(Q8_EINVAL, "%s: workspace must be 16-byte aligned", fn);
   q8::BlockGemmArgs a{};
   a.A = static_cast<const uint8_t*>(A); a.As = As;
   a.W = static_cast<const uint8_t*>(W); a.Ws = Ws;
   a.bias = bias; a.D = D; a.out_dtype = out_dtype;
   a.M = M; a.N = N; a.K = K; a.bn = bn; a.bk = bk;
-  a.workspace = need ? workspace : nullptr;
+  a.workspace = use_ws ? workspace : nullptr;
+  a.workspace_bytes = use_ws ? workspace_bytes : 0;
   return hip_status(q8::launch_blockwise(a, stream), fn);
 }
 

@@ -62,6 +62,21 @@ struct TileParams {
   const int32_t* a_map;    // slot -> A row (nullable)
   const int32_t* c_inv;    // slot -> D row (nullable)
   int E;
+  // dense tiles with the last, part-filled round split in K (gemm_tile with
+  // SPLIT): tile j of that round is computed by an owner over K slabs
+  // [0, split_k) and a helper over [split_k, K/128); the helper's float32
+  // partial goes to part (fragment order, BM*BN floats per tile) and it then
+  // writes token into flag[j]
+  float* part;
+  uint32_t* flag;
+  uint32_t token;          // odd, new for every call
+  int split_k;
+  int64_t split_first;     // workgroups of the whole rounds (tiles not split)
+  int64_t split_lead;      // helpers dispatched ahead of the owners
+  int64_t split_tiles;     // tiles of the last round
+  uint32_t part_bytes;     // extent of part (buffer resource)
+  uint32_t split_wait;     // longest wait of an owner for its helper, in ticks
+                           // of the 100 MHz real-time counter (0: no wait)
 };
 
 __device__ __forceinline__ f32x4 fma4s(f32x4 p, float s, f32x4 acc) {
@@ -168,9 +183,15 @@ struct TileSmem {
 // sm holds stages of at least BM (A) and BN (W) rows; the activation-scale
 // stages, [KSUB][WM][FM/4][16][4], let a lane read its FM row-block scales as
 // FM/4 16-byte vectors, consecutive lanes 16 bytes apart (conflict free).
-template <int BM, int BN, int WM, int WN, int KS, bool GROUPED, bool WSU, bool BIAS>
+// cache-policy operand of the raw buffer load / store builtins: sc1, coherent
+// at agent scope (written through past, and read from past, the XCD's L2)
+constexpr int kSc1 = 16;
+// SPLIT: role 0 computes the whole K range; role 1 (owner) K slabs
+// [0, split_k), then adds the helper's partial of tile slot; role 2 (helper)
+// slabs [split_k, K/128) into that partial.
+template <int BM, int BN, int WM, int WN, int KS, bool GROUPED, bool WSU, bool BIAS, bool SPLIT>
 __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int64_t m_hi, int64_t n0,
-                                          int e, const TileSmem& sm) {
+                                          int e, const TileSmem& sm, int role, int64_t slot) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
@@ -401,23 +422,25 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
     compute(la, lb, ls, wcur);
   };
   const int KT = (int)(K / 128);
-  // the loop used for K blocks of 128, one weight-scale block per wave and up
-  // to 64 K blocks; every other case takes the general loop below
-  auto general_loop = [&]() {
-    load_ws(0);
-    issue(0, sA0, sB0, sS0);
-    for (int kt = 0; kt < KT; ++kt) {
+  // K slabs [ka, kb) into the accumulators. The loop used for K blocks of
+  // 128, one weight-scale block per wave and up to 64 K blocks; every other
+  // case takes the general loop below
+  auto general_loop = [&](int ka, int kb) {
+    load_ws(ka);
+    issue(ka, sA0, sB0, sS0);
+    for (int kt = ka; kt < kb; ++kt) {
       wait_vmem();
       __syncthreads();
-      const bool odd = kt & 1;
-      step(kt, kt + 1 < KT, odd ? sA0 : sA1, odd ? sB0 : sB1, odd ? sS0 : sS1,
+      const bool odd = (kt - ka) & 1;
+      step(kt, kt + 1 < kb, odd ? sA0 : sA1, odd ? sB0 : sB1, odd ? sS0 : sS1,
            odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sS1 : sS0);
     }
   };
+  auto run = [&](int ka, int kb) {
   if constexpr (!(KS == 128 && WSU)) {
-    general_loop();
+    general_loop(ka, kb);
   } else if (KB > 64) {
-    general_loop();
+    general_loop(ka, kb);
   } else {
     // 128-wide K blocks: the last row block of each slab is computed after
     // the slab barrier, behind the LDS reads of the next slab's weight
@@ -490,20 +513,20 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
       // dense tiles: the W rows of slab kt + 1 go out mid-slab (its A rows and
       // scales went out at the last barrier); grouped tiles refill whole slabs
       rows(cur, la, std::integral_constant<int, 0>{}, std::integral_constant<int, NT - FN>{},
-           !GROUPED && kt >= 1 && kt + 1 < KT ? kt + 1 : -1, const_cast<uint8_t*>(nb));
-      if (kt + 1 < KT) {
+           !GROUPED && kt >= ka + 1 && kt + 1 < kb ? kt + 1 : -1, const_cast<uint8_t*>(nb));
+      if (kt + 1 < kb) {
         __builtin_amdgcn_sched_barrier(0);
         wait_vmem();
         __syncthreads();
         // grouped tiles: the refill first (its row-table lookups then retire
         // before the fragment registers fill up)
         if constexpr (GROUPED) {
-          if (kt + 2 < KT) issue(kt + 2, la, lb, ls);
+          if (kt + 2 < kb) issue(kt + 2, la, lb, ls);
         }
         slab_start(nxt, kt + 1, nb, ns);
         av[0] = lds_frag32(na, wm * TM + r16, g);
         if constexpr (!GROUPED) {
-          if (kt + 2 < KT) {
+          if (kt + 2 < kb) {
             issue_a(kt + 2, la);
             issue_s(kt + 2, ls);
           }
@@ -514,15 +537,88 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
       fold(cur, NT - 2);
       fold(cur, NT - 1);
     };
-    issue(0, sA0, sB0, sS0);
+    issue(ka, sA0, sB0, sS0);
     wait_vmem();
     __syncthreads();
-    slab_start(R0, 0, sB0, sS0);
+    slab_start(R0, ka, sB0, sS0);
     av[0] = lds_frag32(sA0, wm * TM + r16, g);
-    if (KT > 1) issue(1, sA1, sB1, sS1);
-    for (int kt = 0; kt < KT; kt += 2) {
+    if (kb - ka > 1) issue(ka + 1, sA1, sB1, sS1);
+    for (int kt = ka; kt < kb; kt += 2) {
       slab(kt, R0, R1, sA0, sB0, sS0, sA1, sB1, sS1);
-      if (kt + 1 < KT) slab(kt + 1, R1, R0, sA1, sB1, sS1, sA0, sB0, sS0);
+      if (kt + 1 < kb) slab(kt + 1, R1, R0, sA1, sB1, sS1, sA0, sB0, sS0);
+    }
+  }
+  };
+
+  // Split tiles: the helper's partial lives in part in fragment order (wave,
+  // row block, column block, lane: 1 KB per store instruction). Its stores
+  // and the owner's loads are agent-coherent (sc1: written through to and
+  // read from past the XCD's L2, which is not coherent with the other XCDs'
+  // L2s), and the helper publishes the partial by writing the call's token
+  // into its flag word once every store has completed.
+  const __amdgpu_buffer_rsrc_t rP = make_rsrc(SPLIT ? p.part : nullptr, SPLIT ? p.part_bytes : 0u);
+  const uint32_t p_off = (uint32_t)slot * (uint32_t)(BM * BN * 4) + (uint32_t)(w * FM * FN * 1024 + lane * 16);
+  uint32_t* const flag = SPLIT ? p.flag + slot : nullptr;
+  if constexpr (!SPLIT) {
+    run(0, KT);
+  } else {
+    // The owner trusts the flag only if it changes to this call's token
+    // while the owner runs: whatever the word held before (a token of an
+    // earlier call, leftovers of other data) can then never pass for the
+    // helper's signal, and the workspace needs no initialisation.
+    __shared__ uint32_t sReady;
+    uint32_t v0 = 0;
+    if (role == 1 && w == 0)
+      v0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+          (int)__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    run(role == 2 ? p.split_k : 0, role == 1 ? p.split_k : KT);
+    bool ready = false;
+    if (role == 1) {
+      // wave 0 waits for the helper, at most split_wait ticks of the 100 MHz
+      // real-time counter; a helper that is not done by then (it could not
+      // get a compute unit, say) leaves the owner to compute the rest of K
+      // itself (the general slab loop: the same products folded in the same
+      // order as the unsplit kernel's, so such a tile comes out as unsplit)
+      if (w == 0) {
+        bool ok = false;
+        if (p.split_wait != 0 && v0 != p.token) {
+          const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+          for (;;) {
+            const uint32_t f = (uint32_t)__builtin_amdgcn_readfirstlane(
+                (int)__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            if (f == p.token) { ok = true; break; }
+            if (__builtin_amdgcn_s_memrealtime() - t0 > p.split_wait) break;
+            __builtin_amdgcn_s_sleep(2);
+          }
+        }
+        if (lane == 0) sReady = ok ? 1u : 0u;
+      }
+      __syncthreads();
+      ready = sReady != 0;
+      if (!ready) general_loop(p.split_k, KT);
+    }
+    if (role == 2) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          __builtin_amdgcn_raw_buffer_store_b128(acc[i][j], rP, p_off, (uint32_t)((i * FN + j) * 1024), kSc1);
+      wait_vmem();
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(flag, p.token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    if (role == 1) {
+      if (ready) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] += __builtin_amdgcn_raw_buffer_load_b128(rP, p_off, (uint32_t)((i * FN + j) * 1024), kSc1);
+      }
+      // the word goes back to zero for the next call (a graph replay passes
+      // the same token again)
+      if (tid == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
@@ -576,13 +672,19 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
   const TileSmem sm{sA0_, sA1_, sB0_, sB1_, sS0_, sS1_}
 
 // One tile shape over the whole output (dense), or over the experts' row
-// ranges (GROUPED).
-template <int BM, int BN, int WM, int WN, int KS, bool GROUPED, bool WSU, bool BIAS>
+// ranges (GROUPED). SPLIT (dense): after split_first workgroups of whole
+// tiles come split_lead helpers, then the owners of the split_tiles tiles of
+// the last round, then the remaining helpers; helpers ahead of the owners are
+// dispatched first, and the later ones take the compute units that the early
+// helpers free while the owners still run.
+template <int BM, int BN, int WM, int WN, int KS, bool GROUPED, bool WSU, bool BIAS, bool SPLIT>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
   Q8_TILE_SMEM(BM, BN, 128 / KS);
   const int lane = threadIdx.x & 63;
   int64_t m_lo, m_hi, n0;
   int e = 0;
+  int role = 0;
+  int64_t slot = 0;
   if constexpr (GROUPED) {
     // (expert, m tile, n tile) of this workgroup from the experts' row
     // offsets, 64 experts at a time across the lanes of every wave (a serial
@@ -631,7 +733,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
     m_hi = m_lo + BM < p.offsets[e + 1] ? m_lo + BM : p.offsets[e + 1];
     n0 = tn * BN;
   } else {
-    const int64_t t = xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n);
+    int64_t b = blockIdx.x;
+    if constexpr (SPLIT) {
+      // split tile j takes the tile that workgroup split_first + j would
+      // take unsplit (same XCD when the counts are multiples of 8)
+      const int64_t c = b - p.split_first;
+      if (c >= 0) {
+        if (c < p.split_lead) { role = 2; slot = c; }
+        else if (c < p.split_lead + p.split_tiles) { role = 1; slot = c - p.split_lead; }
+        else { role = 2; slot = c - p.split_tiles; }
+        b = p.split_first + slot;
+      }
+    }
+    const int64_t t = xcd_remap(b, p.tiles_m * p.tiles_n);
     int64_t tm, tn;
     // four tile-rows per group (measured against eight: 4096x18432x7168
     // 3 % faster, 4096x7168x7168 and 2048x7168x7168 0.5-1 %; sixteen slower)
@@ -640,7 +754,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
     m_hi = m_lo + BM < p.M ? m_lo + BM : p.M;
     n0 = tn * BN;
   }
-  tile_body<BM, BN, WM, WN, KS, GROUPED, WSU, BIAS>(p, m_lo, m_hi, n0, e, sm);
+  tile_body<BM, BN, WM, WN, KS, GROUPED, WSU, BIAS, SPLIT>(p, m_lo, m_hi, n0, e, sm, role, slot);
 }
 
 // ------------------------------------------------------------------------------
@@ -1494,28 +1608,79 @@ hipError_t launch_mid(const TileParams& tp, const MidPlan& pl, int bk, float* pa
 
 constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 4;
 
-template <int KS, bool GROUPED>
-hipError_t launch_tile(const TileParams& tp, int64_t tiles, hipStream_t st) {
-  if (tiles <= 0) return hipSuccess;
-  if (tiles > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+// grid: workgroups (tiles, or for SPLIT the whole-round tiles plus an owner
+// and a helper per split tile)
+template <int KS, bool GROUPED, bool SPLIT = false>
+hipError_t launch_tile(const TileParams& tp, int64_t grid_n, hipStream_t st) {
+  static_assert(!(GROUPED && SPLIT), "the grouped kernel is not split");
+  if (grid_n <= 0) return hipSuccess;
+  if (grid_n > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   constexpr int TN = kBN / kWN;
   // every 16-column block of a wave shares one weight-scale block when the
   // wave's column range never crosses a bn boundary
   const bool wsu = tp.bn % TN == 0;
-  const dim3 grid((unsigned)tiles), block(kWM * kWN * 64);
+  const dim3 grid((unsigned)grid_n), block(kWM * kWN * 64);
   if (!GROUPED && tp.bias) {
     constexpr bool B = !GROUPED;
     if (wsu)
-      hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED, true, B>), grid, block, 0, st, tp);
+      hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED, true, B, SPLIT>), grid, block, 0, st, tp);
     else
-      hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED, false, B>), grid, block, 0, st, tp);
+      hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED, false, B, SPLIT>), grid, block, 0, st, tp);
   } else if (wsu) {
-    hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED, true, false>), grid, block, 0, st, tp);
+    hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED, true, false, SPLIT>), grid, block, 0, st, tp);
   } else {
-    hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED, false, false>), grid, block, 0, st, tp);
+    hipLaunchKernelGGL((gemm_tile<kBM, kBN, kWM, kWN, KS, GROUPED, false, false, SPLIT>), grid, block, 0, st, tp);
   }
   return hipGetLastError();
 }
+
+// Compute units of the current device (0 when there is none), cached per
+// device.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Split of the last round. With one 256x256 workgroup per compute unit, an
+// unsplit launch of T tiles on C units ends with a round of R = T mod C
+// tiles while C - R units idle (4096 x 18432: 1152 tiles, 128 in the fifth
+// round on 256 units). When R <= C / 2 each of those tiles is split in K:
+// its owner takes slabs [0, k), a helper [k, K/128) on one of the idle
+// units. Measured on 4096 x 18432 x 7168: 573 -> 548 us. A fuller last round
+// gains nothing: the chip already runs at its power limit there, and filling
+// the idle units lowers the clock of all (4096 x 7168 x 7168, 192 of 256: 208
+// us unsplit, 219-231 us split with helpers taking up to three tiles each).
+struct SplitPlan {
+  int64_t first, lead, tiles;
+  int k;
+};
+bool split_plan(int64_t tiles, int KT, int cus, SplitPlan& sp) {
+  if (cus <= 0 || KT < 8 || tiles <= 0) return false;
+  const int64_t R = tiles % cus;
+  if (R == 0 || 2 * R > cus) return false;
+  sp.first = tiles - R;
+  sp.lead = R;
+  sp.tiles = R;
+  sp.k = KT / 2 + 1;
+  return true;
+}
+std::atomic<uint32_t> g_split_wait_ticks{20000};  // 200 us
+
+size_t split_part_bytes(int64_t R) { return (size_t)R * kBM * kBN * sizeof(float); }
+size_t split_bytes(int64_t R) { return (split_part_bytes(R) + (size_t)R * 4 + 255) / 256 * 256; }
 
 TileParams make_params(const BlockGemmArgs& a) {
   TileParams tp{};
@@ -1554,6 +1719,17 @@ size_t blockwise_workspace_bytes(int64_t M, int64_t N, int64_t K, int bn, int bk
   return (size_t)pl.S * (size_t)M * (size_t)N * sizeof(float);
 }
 
+void set_split_wait_ticks(uint32_t ticks) { g_split_wait_ticks.store(ticks, std::memory_order_relaxed); }
+
+size_t blockwise_split_bytes(int64_t M, int64_t N, int64_t K, int bn, int bk) {
+  (void)bn; (void)bk;
+  if (M <= kSkinnyMaxM || K % 128 != 0 || N < 1) return 0;
+  SplitPlan sp;
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  if (!split_plan(tiles, (int)(K / 128), device_cus(), sp)) return 0;
+  return split_bytes(sp.tiles);
+}
+
 hipError_t launch_blockwise(const BlockGemmArgs& a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   const TileParams tp = make_params(a);
@@ -1583,6 +1759,23 @@ hipError_t launch_blockwise(const BlockGemmArgs& a, hipStream_t st) {
     return a.bk == 128 ? launch_stream<128>(tp, st) : launch_stream<32>(tp, st);
   }
   const int64_t tiles = tp.tiles_m * tp.tiles_n;
+  SplitPlan sp;
+  if (a.workspace && (uintptr_t)a.workspace % 16 == 0 &&
+      split_plan(tiles, (int)(a.K / 128), device_cus(), sp) && a.workspace_bytes >= split_bytes(sp.tiles)) {
+    static std::atomic<uint32_t> calls{0};
+    TileParams ts = tp;
+    ts.part = static_cast<float*>(a.workspace);
+    ts.flag = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.workspace) + split_part_bytes(sp.tiles));
+    ts.token = (calls.fetch_add(1, std::memory_order_relaxed) << 1) | 1u;
+    ts.split_k = sp.k;
+    ts.split_first = sp.first;
+    ts.split_lead = sp.lead;
+    ts.split_tiles = sp.tiles;
+    ts.part_bytes = (uint32_t)split_part_bytes(sp.tiles);
+    ts.split_wait = g_split_wait_ticks.load(std::memory_order_relaxed);
+    const int64_t grid_n = sp.first + 2 * sp.tiles;
+    return a.bk == 128 ? launch_tile<128, false, true>(ts, grid_n, st) : launch_tile<32, false, true>(ts, grid_n, st);
+  }
   return a.bk == 128 ? launch_tile<128, false>(tp, tiles, st) : launch_tile<32, false>(tp, tiles, st);
 }
 

@@ -36,9 +36,15 @@ struct BlockGemmArgs {
   int64_t w_expert_stride;        // bytes between experts in W
   int64_t ws_expert_stride;       // floats between experts in Ws
   void* workspace;                // split-K partials (dense call), or null
+  size_t workspace_bytes;
 };
 // workspace bytes the dense call needs for this shape (0: none)
 size_t blockwise_workspace_bytes(int64_t M, int64_t N, int64_t K, int bn, int bk);
+// workspace bytes with which the dense call splits the tiles of a last,
+// part-filled round of workgroups on the current device (0: no split); optional
+size_t blockwise_split_bytes(int64_t M, int64_t N, int64_t K, int bn, int bk);
+// longest wait of a split tile's owner for its helper (100 MHz ticks; 0: none)
+void set_split_wait_ticks(uint32_t ticks);
 hipError_t launch_blockwise(const BlockGemmArgs& a, hipStream_t stream);
 hipError_t launch_grouped(const BlockGemmArgs& a, int64_t total_m, int32_t* c_inv_ws,
                           const int32_t* c_map, hipStream_t stream);

@@ -112,14 +112,26 @@ def test_blockwise_validation(q8):
     assert q8._bmm_ws(33, 4096, 7168, 32, 32) == 4 * 33 * 4096 * 4
     assert q8._bmm_ws(64, 4096, 7168, 128, 128) == 4 * 64 * 4096 * 4
     assert q8._bmm_ws(17, 1000, 1024, 128, 128) == 4 * 17 * 1000 * 4
-    for M, N in ((16, 4096), (65, 4096), (33, 1002)):  # other kernels, or N % 4
+    for M, N in ((16, 4096), (33, 1002)):  # other kernels, or N % 4
         assert q8._bmm_ws(M, N, 7168, 128, 128) == 0
+    # more than 64 rows: the optional split of a last round of tiles, sized for
+    # the current device's compute units (none without a device)
+    assert q8._bmm_ws(65, 4096, 7168, 128, 128) % 256 == 0
+    assert q8._bmm_ws(65, 4096, 896, 128, 128) == 0     # fewer than 8 K slabs: never split
     wargs = lambda ws, wsb: (8, 8, 8, 8, p, 8, q8.Q8_BF16, 33, 4096, 7168, 32, 32, ws, wsb, p)
     assert q8._bmm(*wargs(p, 0)) == q8.Q8_EWORKSPACE
     assert "workspace" in q8.last_error()
     assert q8._bmm(*wargs(16, 4 * 33 * 4096 * 4 - 1)) == q8.Q8_EWORKSPACE
     assert q8._bmm(*wargs(20, 4 * 33 * 4096 * 4)) == q8.Q8_EINVAL     # misaligned
     assert "aligned" in q8.last_error()
+
+
+def test_split_wait_setting(q8):
+    assert q8._split_wait(-1) == q8.Q8_EINVAL
+    assert "outside" in q8.last_error()
+    assert q8._split_wait(100001) == q8.Q8_EINVAL
+    assert q8._split_wait(0) == q8.Q8_OK
+    assert q8._split_wait(200) == q8.Q8_OK
 
 
 def test_int8_validation(q8):

@@ -187,3 +187,134 @@ def test_run_twice_identical_and_zero_m():
     e = m.blockwise_scaled_mm(torch.empty((0, 1024), dtype=torch.float8_e4m3fn, device=DEV),
                               Wq.to(DEV), torch.empty((0, 8), device=DEV), Ws.to(DEV))
     assert e.shape == (0, 512)
+
+
+# ---- split of the last round of tiles ------------------------------------------
+def _bmm_capi(aq, As, Wd, Wsd, d, bn, bk, ws=None):
+    """blockwise_scaled_mm through the C ABI with an explicit workspace (None:
+    no workspace, every tile whole)."""
+    m = q8()
+    M, K = aq.shape
+    N = Wd.shape[0]
+    wp, wb = (ws.data_ptr(), ws.numel()) if ws is not None else (None, 0)
+    r = m._bmm(aq.data_ptr(), As.data_ptr(), Wd.data_ptr(), Wsd.data_ptr(), None, d.data_ptr(),
+               m.Q8_BF16, M, N, K, bn, bk, wp, wb, torch.cuda.current_stream().cuda_stream)
+    assert r == 0, m.last_error()
+
+
+def _quantized(M, K, bk, seed):
+    m = q8()
+    x = synth.activations(M, K, "bf16", seed=seed)
+    aq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=DEV)
+    As = torch.empty((M, K // bk), dtype=torch.float32, device=DEV)
+    m.quant_8bit(x.to(DEV), aq, As, bk, EPS, -448.0, 448.0, False)
+    return x, aq, As
+
+
+@pytest.mark.parametrize("bk", [128, 32])
+def test_split_tiles_share_a_workspace_across_calls(bk):
+    """768 x 2816 x 2048: 33 tiles, each split in K between two workgroups.
+    Two calls with different activations on one workspace whose bytes start
+    as random garbage: each output matches the oracle (a stale partial or a
+    flag word that happened to look set would break the second call), and
+    both split calls agree with the unsplit kernel within float32 rounding."""
+    m = q8()
+    M, N, K = 768, 2816, 2048
+    need = m._bmm_ws(M, N, K, bk, bk)
+    assert need >= 33 * 256 * 256 * 4
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device=DEV)
+    Wq, Ws = synth.fp8_block_weights(N, K, bk, bk, seed=11)
+    Wd, Wsd = Wq.to(DEV), Ws.to(DEV)
+    for seed in (21, 22):
+        x, aq, As = _quantized(M, K, bk, seed)
+        d_split = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        d_whole = torch.empty_like(d_split)
+        _bmm_capi(aq, As, Wd, Wsd, d_split, bk, bk, ws)
+        _bmm_capi(aq, As, Wd, Wsd, d_whole, bk, bk, None)
+        sync()
+        ref = oracle_path(x, Wq, Ws, bk, False, bk, bk)[2]
+        assert_gemm_close(d_split, ref, f"split seed={seed}")
+        assert_gemm_close(d_whole, ref, f"whole seed={seed}")
+        diff = (d_split.float() - d_whole.float()).abs()
+        assert float(diff.max()) <= float(d_whole.float().abs().max()) * 2 ** -6
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 18432, 7168), (300, 520, 1024)])
+def test_split_without_wait_equals_unsplit(M, N, K):
+    """With no wait (q8gemm_set_split_wait_us(0)) each tile's first part
+    computes the rest of K itself, folding the same products in the same
+    order as the unsplit kernel: equal bit for bit, also at 4096 x 18432 x
+    7168 (128 split tiles after four whole rounds). The helpers still write
+    their partials and flag words; a later call with the default wait must
+    still match the oracle (small shape) or the unsplit kernel within float32
+    rounding."""
+    m = q8()
+    x, aq, As = _quantized(M, K, 128, 31)
+    Wq, Ws = synth.fp8_block_weights(N, K, 128, 128, seed=31)
+    Wd, Wsd = Wq.to(DEV), Ws.to(DEV)
+    need = m._bmm_ws(M, N, K, 128, 128)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    d_whole = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    d_nowait = torch.empty_like(d_whole)
+    d_split = torch.empty_like(d_whole)
+    _bmm_capi(aq, As, Wd, Wsd, d_whole, 128, 128, None)
+    try:
+        m.set_split_wait_us(0)
+        _bmm_capi(aq, As, Wd, Wsd, d_nowait, 128, 128, ws)
+    finally:
+        m.set_split_wait_us(200)
+    _bmm_capi(aq, As, Wd, Wsd, d_split, 128, 128, ws)
+    sync()
+    assert torch.equal(d_nowait, d_whole)
+    if M <= 512:
+        assert_gemm_close(d_split, oracle_path(x, Wq, Ws, 128, False, 128, 128)[2], "split after no-wait")
+    else:
+        diff = (d_split.float() - d_whole.float()).abs()
+        assert float(diff.max()) <= float(d_whole.float().abs().max()) * 2 ** -6
+
+
+def test_split_tiles_in_a_graph_replay():
+    """The split launch captured in a HIP graph passes the same token on every
+    replay: replays with new activations (and eager calls between them) must
+    each equal an eager call on the same inputs."""
+    m = q8()
+    M, N, K = 640, 1536, 2048
+    Wq, Ws = synth.fp8_block_weights(N, K, 128, 128, seed=41)
+    Wd, Wsd = Wq.to(DEV), Ws.to(DEV)
+    _, aq, As = _quantized(M, K, 128, 41)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        m.blockwise_scaled_mm(aq, Wd, As, Wsd, out=out)  # warm-up: workspace of this stream
+    torch.cuda.current_stream().wait_stream(s)
+    sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m.blockwise_scaled_mm(aq, Wd, As, Wsd, out=out)
+    for seed in (42, 43, 44):
+        _, aq2, As2 = _quantized(M, K, 128, seed)
+        aq.copy_(aq2)
+        As.copy_(As2)
+        eager = m.blockwise_scaled_mm(aq2, Wd, As2, Wsd)
+        sync()
+        g.replay()
+        sync()
+        assert torch.equal(out, eager), f"replay with seed {seed}"
+
+
+def test_split_only_half_empty_last_rounds():
+    """Tiles of the last round are split only when at most half the compute
+    units would run them (a fuller round is left whole): the workspace query
+    says which, per shape."""
+    m = q8()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for M, N in ((4096, 7168), (4096, 18432), (3072, 7168), (1024, 7168), (4096, 4096), (2048, 7168)):
+        tiles = -(-M // 256) * -(-N // 256)
+        R = tiles % cus
+        want = 0 < 2 * R <= cus
+        ws = m._bmm_ws(M, N, 7168, 128, 128)
+        assert (ws > 0) == want, (M, N, cus, ws)
+        if want:
+            assert ws >= R * 256 * 256 * 4 + R * 4

@@ -143,7 +143,13 @@ def test_grouped_single_expert_equals_dense():
     ps = torch.tensor([[T, N, K], [0, N, K], [0, N, K]], dtype=torch.int32, device=DEV)
     d = torch.empty((T, N), dtype=torch.bfloat16, device=DEV)
     m.grouped_blockwise_scaled_mm(d, aq, W.to(DEV), As, Ws.to(DEV), off, ps)
-    dense = m.blockwise_scaled_mm(aq, W[0].to(DEV), As, Ws[0].to(DEV))
+    # the dense call would split its tiles in K (a half-empty last round);
+    # without the wait every tile comes out whole, as the grouped kernel's do
+    try:
+        m.set_split_wait_us(0)
+        dense = m.blockwise_scaled_mm(aq, W[0].to(DEV), As, Ws[0].to(DEV))
+    finally:
+        m.set_split_wait_us(200)
     sync()
     assert torch.equal(d, dense)
 
