@@ -65,8 +65,9 @@ typedef enum {
 const char* q8gemm_last_error(void);
 
 /*
- * Longest time the first part of a split tile (blockwise_scaled_mm with
- * more than 64 rows and a workspace) waits for its second part, in
+ * Longest time the first part of a split tile (blockwise_scaled_mm and
+ * blockwise_scaled_mm_e8m0 with more than 64 rows and a workspace) waits for
+ * its second part, in
  * microseconds, for later calls of this process: default 200, at most
  * 100000. A first part whose second part is not done by then (its
  * workgroup did not get a compute unit in time) computes the rest of K
@@ -201,10 +202,20 @@ int blockwise_scaled_mm(const void* A, const float* As, const void* W, const flo
  * cores (order unspecified); for 17..64 rows with a workspace, K is split into
  * ranges whose float32 partials are summed in ascending range order.
  * workspace: blockwise_scaled_mm_e8m0_workspace_size() bytes, 16-byte
- * aligned: the split-K partials (S x M x N floats; 4 MiB for 64 x 4096 x
- * 7168), 0 for every other shape (then NULL is allowed). Q8_EWORKSPACE if it
- * is needed and missing or short. The contents need no initialisation and are
- * overwritten. Caller owns all buffers; asynchronous on stream.
+ * aligned.
+ * - 17..64 rows: the split-K partials (S x M x N floats; 4 MiB for 64 x 4096
+ *   x 7168); required (Q8_EWORKSPACE if missing or short).
+ * - more than 64 rows, K at least 1024: optional, as for blockwise_scaled_mm:
+ *   a last round of 256 x 256 tiles that fills at most half of the device's
+ *   compute units is split in K between two workgroups each, with R float32
+ *   tile partials and R flag words. A split tile adds two float32 partial
+ *   sums (its outputs can differ from the unsplit ones in the last bits);
+ *   with q8gemm_set_split_wait_us(0) every tile equals the unsplit kernel's
+ *   bit for bit. The size depends on the current device.
+ * - 0 for every other shape (then NULL is allowed).
+ * The contents need no initialisation and are overwritten; calls that may
+ * overlap in time must not share a workspace. Caller owns all buffers;
+ * asynchronous on stream.
  */
 size_t blockwise_scaled_mm_e8m0_workspace_size(int64_t M, int64_t N, int64_t K, int bn);
 int blockwise_scaled_mm_e8m0(const void* A, const uint8_t* As, const void* W, const uint8_t* Ws,

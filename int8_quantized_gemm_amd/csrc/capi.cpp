@@ -159,7 +159,7 @@ int blockwise_scaled_mm(const void* A, const float* As, const void* W, const flo
 
 size_t blockwise_scaled_mm_e8m0_workspace_size(int64_t M, int64_t N, int64_t K, int bn) {
   if (M < 0 || N < 1 || K < 1 || bn < 16 || bn % 16 != 0 || K % 128 != 0) return 0;
-  return q8::blockwise_e8m0_workspace_bytes(M, N, K);
+  return q8::blockwise_e8m0_workspace_bytes(M, N, K) + q8::blockwise_e8m0_split_bytes(M, N, K);
 }
 
 int blockwise_scaled_mm_e8m0(const void* A, const uint8_t* As, const void* W, const uint8_t* Ws,
@@ -179,13 +179,18 @@ int blockwise_scaled_mm_e8m0(const void* A, const uint8_t* As, const void* W, co
   if (!A || !As || !W || !Ws || !D) return fail(Q8_EINVAL, "%s: null pointer", fn);
   if ((uintptr_t)As % 4 != 0 || (uintptr_t)Ws % 4 != 0)
     return fail(Q8_EINVAL, "%s: As and Ws must be 4-byte aligned", fn);
-  const size_t need = blockwise_scaled_mm_e8m0_workspace_size(M, N, K, bn);
+  // the decode split needs its workspace; the split of a last round of tiles
+  // (M > 64) uses one when it is given and large enough
+  const size_t need = q8::blockwise_e8m0_workspace_bytes(M, N, K);
+  const size_t want = need ? 0 : q8::blockwise_e8m0_split_bytes(M, N, K);
   if (need && (!workspace || workspace_bytes < need))
     return fail(Q8_EWORKSPACE, "%s: workspace needs %zu bytes", fn, need);
-  if (need && (uintptr_t)workspace % 16 != 0)
+  const bool use_ws = need || (want && workspace && workspace_bytes >= want);
+  if (use_ws && (uintptr_t)workspace % 16 != 0)
     return fail(Q8_EINVAL, "%s: workspace must be 16-byte aligned", fn);
   q8::MxGemmArgs a{static_cast<const uint8_t*>(A), As, static_cast<const uint8_t*>(W), Ws,
-                   bias, D, out_dtype, M, N, K, bn, need ? workspace : nullptr};
+                   bias, D, out_dtype, M, N, K, bn, use_ws ? workspace : nullptr,
+                   use_ws ? workspace_bytes : 0};
   return hip_status(q8::launch_blockwise_e8m0(a, stream), fn);
 }
 

@@ -183,9 +183,6 @@ struct TileSmem {
 // sm holds stages of at least BM (A) and BN (W) rows; the activation-scale
 // stages, [KSUB][WM][FM/4][16][4], let a lane read its FM row-block scales as
 // FM/4 16-byte vectors, consecutive lanes 16 bytes apart (conflict free).
-// cache-policy operand of the raw buffer load / store builtins: sc1, coherent
-// at agent scope (written through past, and read from past, the XCD's L2)
-constexpr int kSc1 = 16;
 // SPLIT: role 0 computes the whole K range; role 1 (owner) K slabs
 // [0, split_k), then adds the helper's partial of tile slot; role 2 (helper)
 // slabs [split_k, K/128) into that partial.
@@ -580,17 +577,7 @@ __device__ __forceinline__ void tile_body(const TileParams& p, int64_t m_lo, int
       // itself (the general slab loop: the same products folded in the same
       // order as the unsplit kernel's, so such a tile comes out as unsplit)
       if (w == 0) {
-        bool ok = false;
-        if (p.split_wait != 0 && v0 != p.token) {
-          const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-          for (;;) {
-            const uint32_t f = (uint32_t)__builtin_amdgcn_readfirstlane(
-                (int)__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            if (f == p.token) { ok = true; break; }
-            if (__builtin_amdgcn_s_memrealtime() - t0 > p.split_wait) break;
-            __builtin_amdgcn_s_sleep(2);
-          }
-        }
+        const bool ok = split_owner_wait(flag, p.token, v0, p.split_wait);
         if (lane == 0) sReady = ok ? 1u : 0u;
       }
       __syncthreads();
@@ -1634,54 +1621,6 @@ hipError_t launch_tile(const TileParams& tp, int64_t grid_n, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Compute units of the current device (0 when there is none), cached per
-// device.
-int device_cus() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v == 0) {
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) {
-      (void)hipGetLastError();
-      return 0;
-    }
-    cache[dev].store(v, std::memory_order_relaxed);
-  }
-  return v;
-}
-
-// Split of the last round. With one 256x256 workgroup per compute unit, an
-// unsplit launch of T tiles on C units ends with a round of R = T mod C
-// tiles while C - R units idle (4096 x 18432: 1152 tiles, 128 in the fifth
-// round on 256 units). When R <= C / 2 each of those tiles is split in K:
-// its owner takes slabs [0, k), a helper [k, K/128) on one of the idle
-// units. Measured on 4096 x 18432 x 7168: 573 -> 548 us. A fuller last round
-// gains nothing: the chip already runs at its power limit there, and filling
-// the idle units lowers the clock of all (4096 x 7168 x 7168, 192 of 256: 208
-// us unsplit, 219-231 us split with helpers taking up to three tiles each).
-struct SplitPlan {
-  int64_t first, lead, tiles;
-  int k;
-};
-bool split_plan(int64_t tiles, int KT, int cus, SplitPlan& sp) {
-  if (cus <= 0 || KT < 8 || tiles <= 0) return false;
-  const int64_t R = tiles % cus;
-  if (R == 0 || 2 * R > cus) return false;
-  sp.first = tiles - R;
-  sp.lead = R;
-  sp.tiles = R;
-  sp.k = KT / 2 + 1;
-  return true;
-}
-std::atomic<uint32_t> g_split_wait_ticks{20000};  // 200 us
-
-size_t split_part_bytes(int64_t R) { return (size_t)R * kBM * kBN * sizeof(float); }
-size_t split_bytes(int64_t R) { return (split_part_bytes(R) + (size_t)R * 4 + 255) / 256 * 256; }
-
 TileParams make_params(const BlockGemmArgs& a) {
   TileParams tp{};
   tp.A = a.A; tp.As = a.As; tp.W = a.W; tp.Ws = a.Ws;
@@ -1711,6 +1650,61 @@ __global__ void invert_permutation(const int32_t* __restrict__ perm, int64_t n,
 
 }  // namespace
 
+// Compute units of the current device (0 when there is none), cached per
+// device.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Split of the last round. With one 256x256 workgroup per compute unit, an
+// unsplit launch of T tiles on C units ends with a round of R = T mod C
+// tiles while C - R units idle (4096 x 18432: 1152 tiles, 128 in the fifth
+// round on 256 units). When R <= C / 2 each of those tiles is split in K:
+// its owner takes slabs [0, k), a helper [k, K/128) on one of the idle
+// units. Measured on 4096 x 18432 x 7168: 573 -> 548 us. A fuller last round
+// gains nothing: the chip already runs at its power limit there, and filling
+// the idle units lowers the clock of all (4096 x 7168 x 7168, 192 of 256: 208
+// us unsplit, 219-231 us split with helpers taking up to three tiles each).
+bool split_plan(int64_t tiles, int KT, int cus, SplitPlan& sp) {
+  if (cus <= 0 || KT < 8 || tiles <= 0) return false;
+  const int64_t R = tiles % cus;
+  if (R == 0 || 2 * R > cus) return false;
+  sp.first = tiles - R;
+  sp.lead = R;
+  sp.tiles = R;
+  sp.k = KT / 2 + 1;
+  return true;
+}
+namespace {
+std::atomic<uint32_t> g_split_wait_ticks{20000};  // 200 us
+}  // namespace
+
+size_t split_part_bytes(int64_t R) { return (size_t)R * 256 * 256 * sizeof(float); }
+size_t split_bytes(int64_t R) { return (split_part_bytes(R) + (size_t)R * 4 + 255) / 256 * 256; }
+
+void set_split_wait_ticks(uint32_t ticks) { g_split_wait_ticks.store(ticks, std::memory_order_relaxed); }
+
+uint32_t split_wait_ticks() { return g_split_wait_ticks.load(std::memory_order_relaxed); }
+
+uint32_t next_split_token() {
+  static std::atomic<uint32_t> calls{0};
+  return (calls.fetch_add(1, std::memory_order_relaxed) << 1) | 1u;
+}
+
 size_t blockwise_workspace_bytes(int64_t M, int64_t N, int64_t K, int bn, int bk) {
   (void)bn;
   if (K % 128 != 0) return 0;
@@ -1718,8 +1712,6 @@ size_t blockwise_workspace_bytes(int64_t M, int64_t N, int64_t K, int bn, int bk
   if (!mid_plan(M, N, K, bk, pl)) return 0;
   return (size_t)pl.S * (size_t)M * (size_t)N * sizeof(float);
 }
-
-void set_split_wait_ticks(uint32_t ticks) { g_split_wait_ticks.store(ticks, std::memory_order_relaxed); }
 
 size_t blockwise_split_bytes(int64_t M, int64_t N, int64_t K, int bn, int bk) {
   (void)bn; (void)bk;
@@ -1762,17 +1754,16 @@ hipError_t launch_blockwise(const BlockGemmArgs& a, hipStream_t st) {
   SplitPlan sp;
   if (a.workspace && (uintptr_t)a.workspace % 16 == 0 &&
       split_plan(tiles, (int)(a.K / 128), device_cus(), sp) && a.workspace_bytes >= split_bytes(sp.tiles)) {
-    static std::atomic<uint32_t> calls{0};
     TileParams ts = tp;
     ts.part = static_cast<float*>(a.workspace);
     ts.flag = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.workspace) + split_part_bytes(sp.tiles));
-    ts.token = (calls.fetch_add(1, std::memory_order_relaxed) << 1) | 1u;
+    ts.token = next_split_token();
     ts.split_k = sp.k;
     ts.split_first = sp.first;
     ts.split_lead = sp.lead;
     ts.split_tiles = sp.tiles;
     ts.part_bytes = (uint32_t)split_part_bytes(sp.tiles);
-    ts.split_wait = g_split_wait_ticks.load(std::memory_order_relaxed);
+    ts.split_wait = split_wait_ticks();
     const int64_t grid_n = sp.first + 2 * sp.tiles;
     return a.bk == 128 ? launch_tile<128, false, true>(ts, grid_n, st) : launch_tile<32, false, true>(ts, grid_n, st);
   }

@@ -63,6 +63,19 @@ struct MxParams {
   int d_vec4;
   uint32_t a_bytes, as_bytes;
   int64_t tiles_m, tiles_n;
+  // last round split in K (gemm_tile_mx with SPLIT): the first split_first
+  // workgroups take whole tiles, then split_lead helpers, the owners of the
+  // split_tiles tiles of the last round, and the remaining helpers; owners
+  // take K slabs [0, split_k), helpers the rest, their float32 partials going
+  // to part (fragment order, 256 * 256 floats per tile) and published by
+  // writing token into the tile's flag word
+  float* part;
+  uint32_t* flag;
+  uint32_t token;
+  int split_k;
+  int64_t split_first, split_lead, split_tiles;
+  uint32_t part_bytes;
+  uint32_t split_wait;  // longest wait of an owner, in 100 MHz ticks (0: none)
 };
 
 __device__ __forceinline__ f32x4 mfma_mx(const i32x8& w, const i32x8& a, const f32x4& c,
@@ -110,7 +123,10 @@ __device__ __forceinline__ void store4_mx(const MxParams& p, int64_t row, int64_
 }
 
 // ------------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN>
+// SPLIT: the launch splits the tiles of its last round in K (see MxParams);
+// an owner that stops waiting for its helper runs on through the rest of K,
+// so that tile comes out exactly as unsplit.
+template <int BM, int BN, int WM, int WN, bool SPLIT>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_mx(MxParams p) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -131,7 +147,24 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_mx(MxParams p) {
   const int64_t M = p.M, N = p.N, K = p.K;
   const int KB = p.KB;
 
-  const int64_t t = xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n);
+  const int KT = (int)(K / 128);
+  int64_t b = blockIdx.x;
+  int role = 0, ka = 0, kb = KT;  // role 0: whole K, 1: owner, 2: helper
+  int64_t slot = 0;
+  if constexpr (SPLIT) {
+    // split tile j takes the tile that workgroup split_first + j would take
+    // unsplit (same XCD when the counts are multiples of 8)
+    const int64_t c = b - p.split_first;
+    if (c >= 0) {
+      if (c < p.split_lead) { role = 2; slot = c; }
+      else if (c < p.split_lead + p.split_tiles) { role = 1; slot = c - p.split_lead; }
+      else { role = 2; slot = c - p.split_tiles; }
+      b = p.split_first + slot;
+      if (role == 1) kb = p.split_k;
+      else ka = p.split_k;
+    }
+  }
+  const int64_t t = xcd_remap(b, p.tiles_m * p.tiles_n);
   int64_t tm, tn;
   grouped_order(t, p.tiles_m, p.tiles_n, 8, tm, tn);
   const int64_t m_lo = tm * BM, n0 = tn * BN;
@@ -196,9 +229,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_mx(MxParams p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](int kt, bool refill, uint8_t* __restrict__ na, uint8_t* __restrict__ nb,
+  // slab kt lives in stage st (0 or 1, alternating from the first slab run)
+  auto step = [&](int kt, int st, bool refill, uint8_t* __restrict__ na, uint8_t* __restrict__ nb,
                   const uint8_t* __restrict__ la, const uint8_t* __restrict__ lb) {
-    const int st = kt & 1;
     if (refill) {
       issue(kt + 1, na, nb);
       issue_scales(kt + 1, st ^ 1);
@@ -234,14 +267,76 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_mx(MxParams p) {
     }
   };
 
-  const int KT = (int)(K / 128);
-  issue(0, sA0, sB0);
-  issue_scales(0, 0);
-  for (int kt = 0; kt < KT; ++kt) {
-    wait_vmem();
-    __syncthreads();
-    const bool odd = kt & 1;
-    step(kt, kt + 1 < KT, odd ? sA0 : sA1, odd ? sB0 : sB1, odd ? sA1 : sA0, odd ? sB1 : sB0);
+  // K slabs [k0, k1) into the accumulators
+  auto run = [&](int k0, int k1) {
+    issue(k0, sA0, sB0);
+    issue_scales(k0, 0);
+    for (int kt = k0; kt < k1; ++kt) {
+      wait_vmem();
+      __syncthreads();
+      const int odd = (kt - k0) & 1;
+      step(kt, odd, kt + 1 < k1, odd ? sA0 : sA1, odd ? sB0 : sB1, odd ? sA1 : sA0, odd ? sB1 : sB0);
+    }
+  };
+  if constexpr (!SPLIT) {
+    run(0, KT);
+  } else {
+    // The partial of a split tile lives in part in fragment order (wave, row
+    // block, column block, lane: 1 KB per store instruction), written and
+    // read coherently at agent scope (sc1).
+    __shared__ uint32_t sReady;
+    uint32_t* const flag = p.flag + slot;
+    uint32_t v0 = 0;
+    if (role == 1 && w == 0)
+      v0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+          (int)__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    // An owner whose helper is not done in time runs on through the rest of
+    // K (a second pass of the same loop): the same MFMA chain as the unsplit
+    // kernel, so the tile comes out exactly as unsplit.
+    bool ready = false;
+    int k0 = ka, k1 = kb;
+    for (;;) {
+      run(k0, k1);
+      if (role != 1 || k1 == KT) break;
+      if (w == 0) {
+        const bool ok = split_owner_wait(flag, p.token, v0, p.split_wait);
+        if (lane == 0) sReady = ok ? 1u : 0u;
+      }
+      __syncthreads();
+      ready = sReady != 0;
+      if (ready) break;
+      k0 = kb;
+      k1 = KT;
+    }
+    const __amdgpu_buffer_rsrc_t rP = make_rsrc(p.part, p.part_bytes);
+    const uint32_t p_off = (uint32_t)slot * (uint32_t)(BM * BN * 4) + (uint32_t)(w * FM * FN * 1024 + lane * 16);
+    if (role == 2) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          __builtin_amdgcn_raw_buffer_store_b128(acc[i][j], rP, p_off, (uint32_t)((i * FN + j) * 1024), kSc1);
+      wait_vmem();
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(flag, p.token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    if (role == 1) {
+      if (ready) {
+        // one row block's partials at a time (all of them in flight at once
+        // would need 128 more registers)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] += __builtin_amdgcn_raw_buffer_load_b128(rP, p_off, (uint32_t)((i * FN + j) * 1024), kSc1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // the word goes back to zero for the next call (a graph replay passes
+      // the same token again)
+      if (tid == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 
   const bool bf16 = p.out_bf16 != 0, vec = p.d_vec4 != 0;
@@ -719,6 +814,14 @@ size_t blockwise_e8m0_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return (size_t)pl.S * (size_t)M * (size_t)N * sizeof(float);
 }
 
+size_t blockwise_e8m0_split_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 64 || K % 128 != 0 || N < 1) return 0;
+  SplitPlan sp;
+  const int64_t tiles = ((M + kMxBM - 1) / kMxBM) * ((N + kMxBN - 1) / kMxBN);
+  if (!split_plan(tiles, (int)(K / 128), device_cus(), sp)) return 0;
+  return split_bytes(sp.tiles);
+}
+
 hipError_t launch_blockwise_e8m0(const MxGemmArgs& a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   MxParams p{};
@@ -752,7 +855,23 @@ hipError_t launch_blockwise_e8m0(const MxGemmArgs& a, hipStream_t st) {
   }
   const int64_t tiles = p.tiles_m * p.tiles_n;
   if (tiles > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((gemm_tile_mx<kMxBM, kMxBN, kMxWM, kMxWN>), dim3((unsigned)tiles),
+  SplitPlan sp;
+  if (a.workspace && (uintptr_t)a.workspace % 16 == 0 && split_plan(tiles, (int)(a.K / 128), device_cus(), sp) &&
+      a.workspace_bytes >= split_bytes(sp.tiles)) {
+    p.part = static_cast<float*>(a.workspace);
+    p.flag = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.workspace) + split_part_bytes(sp.tiles));
+    p.token = next_split_token();
+    p.split_k = sp.k;
+    p.split_first = sp.first;
+    p.split_lead = sp.lead;
+    p.split_tiles = sp.tiles;
+    p.part_bytes = (uint32_t)split_part_bytes(sp.tiles);
+    p.split_wait = split_wait_ticks();
+    hipLaunchKernelGGL((gemm_tile_mx<kMxBM, kMxBN, kMxWM, kMxWN, true>),
+                       dim3((unsigned)(sp.first + 2 * sp.tiles)), dim3(kMxWM * kMxWN * 64), 0, st, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((gemm_tile_mx<kMxBM, kMxBN, kMxWM, kMxWN, false>), dim3((unsigned)tiles),
                      dim3(kMxWM * kMxWN * 64), 0, st, p);
   return hipGetLastError();
 }

@@ -45,6 +45,22 @@ size_t blockwise_workspace_bytes(int64_t M, int64_t N, int64_t K, int bn, int bk
 size_t blockwise_split_bytes(int64_t M, int64_t N, int64_t K, int bn, int bk);
 // longest wait of a split tile's owner for its helper (100 MHz ticks; 0: none)
 void set_split_wait_ticks(uint32_t ticks);
+uint32_t split_wait_ticks();
+// odd, new for every call
+uint32_t next_split_token();
+// compute units of the current device (0 without one), cached per device
+int device_cus();
+// Split of the last round of 256 x 256 tiles (both block-scaled tile
+// kernels): the R = tiles mod C tiles of a last round that fills at most half
+// of the C compute units are each split in K between an owner (slabs
+// [0, k)), and a helper (the rest).
+struct SplitPlan {
+  int64_t first, lead, tiles;
+  int k;
+};
+bool split_plan(int64_t tiles, int KT, int cus, SplitPlan& sp);
+size_t split_part_bytes(int64_t R);  // float32 partials of R tiles
+size_t split_bytes(int64_t R);       // the partials and R flag words
 hipError_t launch_blockwise(const BlockGemmArgs& a, hipStream_t stream);
 hipError_t launch_grouped(const BlockGemmArgs& a, int64_t total_m, int32_t* c_inv_ws,
                           const int32_t* c_map, hipStream_t stream);
@@ -55,9 +71,13 @@ struct MxGemmArgs {
   const void* bias; void* D; q8_dtype out_dtype;
   int64_t M, N, K; int bn;
   void* workspace;  // split-K partials (17..64 rows), or null
+  size_t workspace_bytes;
 };
 // workspace bytes the E8M0 call needs for this shape (0: none)
 size_t blockwise_e8m0_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// workspace bytes with which the E8M0 call splits a last, half-empty round of
+// tiles on the current device (0: no split); optional
+size_t blockwise_e8m0_split_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_blockwise_e8m0(const MxGemmArgs& a, hipStream_t stream);
 
 // ---- INT8 GEMM ----------------------------------------------------------------

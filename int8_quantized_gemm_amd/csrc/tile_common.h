@@ -55,6 +55,29 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t total) {
   return x < rem ? x * (base + 1) + i : rem * (base + 1) + (x - rem) * base + i;
 }
 
+// Cache-policy operand of the raw buffer load / store builtins: sc1, coherent
+// at agent scope (written through past, and read from past, the XCD's L2,
+// which is not coherent with the other XCDs' L2s).
+constexpr int kSc1 = 16;
+
+// Split tiles of a last round (the tile kernels' SPLIT instances): the owner
+// of a tile read its flag word (v0) when it started; after its own K slabs it
+// takes the helper's partial only if the word changes to this call's token
+// while it waits, at most wait_ticks of the 100 MHz real-time counter (0: it
+// never waits). Called by one wave; the result is wave-uniform.
+__device__ __forceinline__ bool split_owner_wait(uint32_t* flag, uint32_t token, uint32_t v0,
+                                                 uint32_t wait_ticks) {
+  if (wait_ticks == 0 || v0 == token) return false;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
+    const uint32_t f = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (f == token) return true;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > wait_ticks) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
 // Logical tile id -> (tm, tn), walking GM tile-rows at a time so that the
 // tiles resident together share A rows and W rows in L2.
 __device__ __forceinline__ void grouped_order(int64_t t, int64_t tiles_m, int64_t tiles_n, int gm,

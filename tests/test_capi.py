@@ -198,8 +198,12 @@ def test_e8m0_gemm_validation(q8):
     # 17..64 rows split K: float32 partials of 4 ranges in the workspace
     assert q8._bmm8_ws(64, 4096, 7168, 32) == 4 * 64 * 4096 * 4
     assert q8._bmm8_ws(17, 1000, 1024, 32) == 4 * 17 * 1000 * 4
-    for M, N in ((16, 4096), (65, 4096), (33, 1002)):
+    for M, N in ((16, 4096), (33, 1002)):
         assert q8._bmm8_ws(M, N, 7168, 32) == 0
+    # more than 64 rows: the optional split of a last round of tiles, sized for
+    # the current device's compute units (none without a device)
+    assert q8._bmm8_ws(65, 4096, 7168, 32) % 256 == 0
+    assert q8._bmm8_ws(65, 4096, 896, 32) == 0
     wargs = lambda ws, wsb: (16, 16, 16, 16, p, 16, q8.Q8_BF16, 33, 4096, 7168, 32, ws, wsb, p)
     assert q8._bmm8(*wargs(p, 0)) == q8.Q8_EWORKSPACE
     assert q8._bmm8(*wargs(32, 4 * 33 * 4096 * 4 - 1)) == q8.Q8_EWORKSPACE

@@ -131,3 +131,105 @@ def test_quant_then_gemm_pipeline():
     aq, so = oq.per_token_group(x.float().numpy(), 32, EPS, -448.0, 448.0, True, "e4m3")
     ref = og.blockwise_scaled_mm_e8m0(aq, oq.e8m0_bytes(so), Wq.numpy(), Wsb.numpy(), 32)
     assert_gemm_close(d, ref, "quant + e8m0 gemm")
+
+
+# ---- split of the last round of tiles ------------------------------------------
+def _mx_capi(aq, asb, Wd, Wsd, d, bn, ws=None):
+    """blockwise_scaled_mm_e8m0 through the C ABI with an explicit workspace
+    (None: no workspace, every tile whole)."""
+    m = q8()
+    M, K = aq.shape
+    N = Wd.shape[0]
+    wp, wb = (ws.data_ptr(), ws.numel()) if ws is not None else (None, 0)
+    r = m._bmm8(aq.data_ptr(), asb.data_ptr(), Wd.data_ptr(), Wsd.data_ptr(), None, d.data_ptr(),
+                m.Q8_BF16, M, N, K, bn, wp, wb, torch.cuda.current_stream().cuda_stream)
+    assert r == 0, m.last_error()
+
+
+def test_e8m0_split_tiles_share_a_workspace_across_calls():
+    """768 x 2816 x 2048: 33 tiles, each split in K between an owner and a
+    helper. Two calls with different activations on one workspace whose bytes
+    start as random garbage: each matches the oracle, and each agrees with the
+    unsplit kernel within float32 rounding."""
+    m = q8()
+    M, N, K, bn = 768, 2816, 2048, 32
+    need = m._bmm8_ws(M, N, K, bn)
+    assert need >= 33 * 256 * 256 * 4
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device=DEV)
+    Wq, Wsb = synth.fp8_block_weights_e8m0(N, K, bn, 32, seed=12)
+    Wd, Wsd = Wq.to(DEV), Wsb.to(DEV)
+    for seed in (51, 52):
+        x, aq, asb = _act(M, K, seed=seed)
+        aqd, asd = torch.from_numpy(aq).to(DEV), torch.from_numpy(asb).to(DEV)
+        d_split = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        d_whole = torch.empty_like(d_split)
+        _mx_capi(aqd, asd, Wd, Wsd, d_split, bn, ws)
+        _mx_capi(aqd, asd, Wd, Wsd, d_whole, bn, None)
+        sync()
+        ref = og.blockwise_scaled_mm_e8m0(aq, asb, Wq.numpy(), Wsb.numpy(), bn)
+        assert_gemm_close(d_split, ref, f"e8m0 split seed={seed}")
+        assert_gemm_close(d_whole, ref, f"e8m0 whole seed={seed}")
+        diff = (d_split.float() - d_whole.float()).abs()
+        assert float(diff.max()) <= float(d_whole.float().abs().max()) * 2 ** -6
+
+
+@pytest.mark.parametrize("M,N,K", [(3072, 7168, 7168), (300, 520, 1024)])
+def test_e8m0_split_without_wait_equals_unsplit(M, N, K):
+    """With no wait each split tile's owner runs on through the rest of K, the
+    same MFMA chain as the unsplit kernel: equal bit for bit (3072 x 7168 x
+    7168: 80 split tiles after one whole round). A later call with the default
+    wait agrees with the unsplit kernel within float32 rounding."""
+    m = q8()
+    bn = 32
+    x, aq, asb = _act(M, K, seed=61)
+    Wq, Wsb = synth.fp8_block_weights_e8m0(N, K, bn, 32, seed=61)
+    Wd, Wsd = Wq.to(DEV), Wsb.to(DEV)
+    aqd, asd = torch.from_numpy(aq).to(DEV), torch.from_numpy(asb).to(DEV)
+    need = m._bmm8_ws(M, N, K, bn)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    d_whole = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    d_nowait = torch.empty_like(d_whole)
+    d_split = torch.empty_like(d_whole)
+    _mx_capi(aqd, asd, Wd, Wsd, d_whole, bn, None)
+    try:
+        m.set_split_wait_us(0)
+        _mx_capi(aqd, asd, Wd, Wsd, d_nowait, bn, ws)
+    finally:
+        m.set_split_wait_us(200)
+    _mx_capi(aqd, asd, Wd, Wsd, d_split, bn, ws)
+    sync()
+    assert torch.equal(d_nowait, d_whole)
+    diff = (d_split.float() - d_whole.float()).abs()
+    assert float(diff.max()) <= float(d_whole.float().abs().max()) * 2 ** -6
+
+
+def test_e8m0_split_tiles_in_a_graph_replay():
+    """The split launch captured in a HIP graph: replays with new activations
+    (and eager calls between them) each equal an eager call on the same
+    inputs."""
+    m = q8()
+    M, N, K, bn = 640, 1536, 2048, 32
+    Wq, Wsb = synth.fp8_block_weights_e8m0(N, K, bn, 32, seed=71)
+    Wd, Wsd = Wq.to(DEV), Wsb.to(DEV)
+    _, aq, asb = _act(M, K, seed=71)
+    aqd, asd = torch.from_numpy(aq).to(DEV), torch.from_numpy(asb).to(DEV)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        m.blockwise_scaled_mm_e8m0(aqd, Wd, asd, Wsd, block_n=bn, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m.blockwise_scaled_mm_e8m0(aqd, Wd, asd, Wsd, block_n=bn, out=out)
+    for seed in (72, 73, 74):
+        _, aq2, asb2 = _act(M, K, seed=seed)
+        aqd.copy_(torch.from_numpy(aq2).to(DEV))
+        asd.copy_(torch.from_numpy(asb2).to(DEV))
+        eager = m.blockwise_scaled_mm_e8m0(aqd.clone(), Wd, asd.clone(), Wsd, block_n=bn)
+        sync()
+        g.replay()
+        sync()
+        assert torch.equal(out, eager), f"replay with seed {seed}"
