@@ -663,33 +663,72 @@ __device__ __forceinline__ float silu_h_bf16(float g, const float* __restrict__ 
 // lanes adjacent in one wave), over a grid of at most two workgroups per CU
 // striding in whole workgroups, so each workgroup builds the table once
 // (two per CU measured 2 % faster than one at [4096, 2 x 7168]; two vectors
-// per thread and iteration were 15 % slower).
+// per thread and iteration were 15 % slower). With a mask (E = M / max_m
+// blocks, at most kSiluMaskMaxE) the workgroups stride over the live rows
+// only: live row r is row r - pre[e] of block e, pre the exclusive prefix sum
+// of the blocks' valid-row counts (clamped to [0, max_m]), found by a binary
+// search of pre in LDS.
+constexpr int kSiluMaskMaxE = 1024;
 template <bool FP8, int UE, int TPG>
 __global__ __launch_bounds__(kSiluThreads) void quant_silu_bf16_table(
     const void* __restrict__ x, int64_t M, int64_t K, int64_t ld_x, uint8_t* __restrict__ q,
     float* __restrict__ s, const int32_t* __restrict__ masked_m, uint32_t max_m, float eps,
     float qmin, float qmax) {
   __shared__ float tab[kSiluTable];
+  __shared__ uint32_t pre[kSiluMaskMaxE + 1];
   for (int i = threadIdx.x; i < kSiluTable; i += kSiluThreads) {
     const uint32_t e = kSiluExpLo + ((uint32_t)i >> 7 & 31u);
     const uint32_t b = ((uint32_t)i >> 12 << 15) | (e << 7) | ((uint32_t)i & 127u);
     tab[i] = silu_h(__uint_as_float(b << 16));
   }
-  __syncthreads();
   const uint32_t vpr = (uint32_t)(K / 16);
-  const uint32_t total = (uint32_t)(M * vpr);
+  const uint32_t E = masked_m ? (uint32_t)(M / max_m) : 0u;
+  if (masked_m && threadIdx.x < kWave) {
+    // one wave: inclusive scan of 64 counts at a time
+    const int lane = (int)threadIdx.x;
+    uint32_t carry = 0;
+    if (lane == 0) pre[0] = 0;
+    for (uint32_t c = 0; c < E; c += kWave) {
+      const uint32_t e = c + (uint32_t)lane;
+      int32_t n = e < E ? masked_m[e] : 0;
+      n = n < 0 ? 0 : ((uint32_t)n > max_m ? (int32_t)max_m : n);
+      uint32_t incl = (uint32_t)n;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)incl, off, kWave);
+        if (lane >= off) incl += y;
+      }
+      if (e < E) pre[e + 1] = carry + incl;
+      carry += (uint32_t)__shfl((int)incl, kWave - 1, kWave);
+    }
+  }
+  __syncthreads();
+  const uint32_t rows = masked_m ? pre[E] : (uint32_t)M;
+  const uint32_t total = rows * vpr;
   for (uint32_t base = blockIdx.x * kSiluThreads; base < total; base += gridDim.x * kSiluThreads) {
-    const uint32_t v = base + threadIdx.x;
-    const uint32_t vv = v < total ? v : total - 1;
-    const uint32_t row = vv / vpr;
-    const bool live = v < total && row_live(masked_m, max_m, row);
+    const uint32_t vl = base + threadIdx.x;
+    const bool live = vl < total;
     if (__ballot(live) == 0) continue;  // wave-uniform
+    const uint32_t vc = live ? vl : total - 1;
+    uint32_t row = vc / vpr;
+    const uint32_t col = vc - row * vpr;
+    if (masked_m) {
+      // block e of live row `row`: the last e with pre[e] <= row
+      uint32_t lo = 0, hi = E;  // pre[lo] <= row < pre[hi]
+      while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (pre[mid] <= row) lo = mid;
+        else hi = mid;
+      }
+      row = lo * max_m + (row - pre[lo]);
+    }
+    const uint32_t v = row * vpr + col;
     // dead lanes take part in the shuffles with a = 0; y is read on live
     // lanes only
     float y[2][8];
     float a = 0.0f;
     if (live) {
-      const int64_t off = (int64_t)row * ld_x + (int64_t)(vv - row * vpr) * 16;
+      const int64_t off = (int64_t)row * ld_x + (int64_t)col * 16;
       float u[2][8];
       load8<Q8_BF16>(x, off, y[0]);
       load8<Q8_BF16>(x, off + 8, y[1]);
@@ -731,7 +770,8 @@ hipError_t dispatch_fused(const QuantArgs& a, hipStream_t st) {
   const bool wave = g >= 16 && g <= 512 && (g & (g - 1)) == 0 && total < 0xFFFF0000LL &&
                     (uintptr_t)a.x % 16 == 0 && (uintptr_t)q % 16 == 0 &&
                     (a.ld_x * esz) % 16 == 0 && (a.K * esz) % 16 == 0;
-  if constexpr (SILU && XT == Q8_BF16) if (wave && a.M * a.K >= kSiluTableMinElems) {
+  const bool mask_fits = !a.masked_m || a.M / (int64_t)max_m <= kSiluMaskMaxE;
+  if constexpr (SILU && XT == Q8_BF16) if (wave && mask_fits && a.M * a.K >= kSiluTableMinElems) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)

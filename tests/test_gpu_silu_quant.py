@@ -115,6 +115,24 @@ def test_masked_rows_table_path():
     assert np.all(qg[~valid].view(np.uint8) == 0x5A) and np.all(sg[~valid] == -7.0)
 
 
+@pytest.mark.parametrize("E,max_m", [(300, 16), (1100, 4)])
+def test_masked_many_blocks_table_path(E, max_m):
+    """Many masked blocks on the table path: more than one 64-count chunk of
+    the live-row prefix sum (300 blocks), counts above the block size, zero
+    and negative counts, and more blocks than the live-row table holds (1100:
+    the kernel that tests every row). Untouched rows keep their bytes."""
+    K, g = 1024, 128
+    rng = np.random.default_rng(E)
+    mm = rng.integers(-3, max_m + 4, size=E).astype(np.int32)
+    mm[:4] = [0, max_m, max_m + 5, -1]
+    x = synth.activations(E * max_m, 2 * K, "bf16", seed=E).reshape(E, max_m, -1)
+    qg, sg = _run(x.to(DEV), K, g, masked_m=torch.from_numpy(mm).to(DEV))
+    qo, so, valid = _oracle(x, g, masked_m=np.clip(mm, 0, max_m), max_m=max_m)
+    qg, sg = qg.reshape(E * max_m, K), sg.reshape(E * max_m, -1)
+    assert np.array_equal(qg[valid], qo[valid]) and np.array_equal(sg[valid], so[valid])
+    assert np.all(qg[~valid].view(np.uint8) == 0x5A) and np.all(sg[~valid] == -7.0)
+
+
 @pytest.mark.parametrize("xdt", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("g,ue,int8", [(128, False, False), (32, True, False), (16, False, False),
                                        (512, False, False), (128, False, True), (96, False, False),
