@@ -10,7 +10,7 @@
 //   1. moe_count  — one workgroup per chunk of 256 flat entries builds the
 //                   chunk's per-expert histogram in LDS (counts are order
 //                   independent);
-//   2. moe_scan   — one thread per expert scans its counts over the chunks
+//   2. moe_scan   — the experts' counts are scanned over the chunks
 //                   (exclusive, from LDS slabs), then the per-expert totals
 //                   are scanned over the experts into expert_offsets and
 //                   problem sizes, and the chunk bases are shifted by the
@@ -44,8 +44,17 @@ __global__ __launch_bounds__(kChunk) void moe_count(const int32_t* __restrict__ 
 }
 
 // Chunk counts are staged through LDS a slab at a time (coalesced loads by
-// every thread) so that each expert's thread scans from LDS instead of
-// chasing dependent global loads.
+// every thread) so that each expert's column is scanned from LDS instead of
+// through dependent global loads. A count matrix that fits one slab (up to
+// 8192 counts: 4096 tokens x top-8 over 64 experts) stays in LDS until the
+// experts' offsets are added and is written once, and each expert's column
+// is scanned by P = 1024 / E threads (P = 16 for 64 experts): every thread
+// sums its run of rows, the runs' sums are added up in order for its base,
+// and it rewrites its rows as exclusive prefixes, so the chain of dependent
+// LDS accesses is a run of rows long instead of a whole column (measured
+// 18.3 -> 16.4 us for the three routing kernels at 4096 x top-8 of 64).
+// Larger matrices go slab by slab, one thread per expert (the split scan's
+// extra barrier per slab measured slower there).
 constexpr int kSlabInts = 8192;  // 32 KB of LDS
 
 __global__ __launch_bounds__(kScanThreads) void moe_scan(int32_t* __restrict__ counts,
@@ -54,47 +63,88 @@ __global__ __launch_bounds__(kScanThreads) void moe_scan(int32_t* __restrict__ c
                                                          int32_t* __restrict__ ps1,
                                                          int32_t* __restrict__ ps2) {
   __shared__ int32_t tot[kScanThreads];
+  __shared__ int32_t carry[kScanThreads];    // per expert: its total count
+  __shared__ int32_t part_sum[kScanThreads];  // [part][expert]
   __shared__ int32_t slab[kSlabInts];
-  const int e = threadIdx.x;
+  const int tid = threadIdx.x;
   const int64_t rows_per_slab = kSlabInts / E;
-  int32_t run = 0;
+  const bool one_slab = nchunks <= rows_per_slab;
   // pass 1: per-expert exclusive scan over the chunks (relative bases)
-  for (int64_t c0 = 0; c0 < nchunks; c0 += rows_per_slab) {
-    const int64_t rows = nchunks - c0 < rows_per_slab ? nchunks - c0 : rows_per_slab;
-    for (int64_t i = threadIdx.x; i < rows * E; i += kScanThreads) slab[i] = counts[c0 * E + i];
+  if (one_slab) {
+    const int parts = kScanThreads / E;  // E <= kScanThreads
+    const int e = tid % E, part = tid / E;
+    const bool active = part < parts;
+    const int64_t rows = nchunks;
+    for (int64_t i = tid; i < rows * E; i += kScanThreads) slab[i] = counts[i];
     __syncthreads();
-    if (e < E) {
-      for (int64_t r = 0; r < rows; ++r) {
+    const int64_t rpp = (rows + parts - 1) / parts;
+    const int64_t r0 = part * rpp, r1 = r0 + rpp < rows ? r0 + rpp : rows;
+    int32_t sum = 0;
+    if (active)
+      for (int64_t r = r0; r < r1; ++r) sum += slab[r * E + e];
+    if (active) part_sum[part * E + e] = sum;
+    __syncthreads();
+    if (active) {
+      int32_t run = 0;
+      for (int q = 0; q < part; ++q) run += part_sum[q * E + e];
+      for (int64_t r = r0; r < r1; ++r) {
         const int32_t v = slab[r * E + e];
         slab[r * E + e] = run;
         run += v;
       }
     }
+    if (tid < E) {
+      int32_t t = 0;
+      for (int q = 0; q < parts; ++q) t += part_sum[q * E + tid];
+      carry[tid] = t;
+    }
     __syncthreads();
-    for (int64_t i = threadIdx.x; i < rows * E; i += kScanThreads) counts[c0 * E + i] = slab[i];
+  } else {
+    int32_t run = 0;
+    for (int64_t c0 = 0; c0 < nchunks; c0 += rows_per_slab) {
+      const int64_t rows = nchunks - c0 < rows_per_slab ? nchunks - c0 : rows_per_slab;
+      for (int64_t i = tid; i < rows * E; i += kScanThreads) slab[i] = counts[c0 * E + i];
+      __syncthreads();
+      if (tid < E) {
+        for (int64_t r = 0; r < rows; ++r) {
+          const int32_t v = slab[r * E + tid];
+          slab[r * E + tid] = run;
+          run += v;
+        }
+      }
+      __syncthreads();
+      for (int64_t i = tid; i < rows * E; i += kScanThreads) counts[c0 * E + i] = slab[i];
+      __syncthreads();
+    }
+    if (tid < E) carry[tid] = run;
     __syncthreads();
   }
-  tot[e] = e < E ? run : 0;
+  const int32_t run = tid < E ? carry[tid] : 0;  // the expert's total
+  tot[tid] = run;
   __syncthreads();
   // inclusive Hillis-Steele scan over the per-expert totals
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int32_t v = e >= off ? tot[e - off] : 0;
+  for (int off = 1; off < E; off <<= 1) {
+    const int32_t v = tid >= off ? tot[tid - off] : 0;
     __syncthreads();
-    tot[e] += v;
+    tot[tid] += v;
     __syncthreads();
   }
-  if (e < E) {
-    const int32_t base = tot[e] - run;  // exclusive prefix
-    offsets[e] = base;
-    if (e == E - 1) offsets[E] = tot[e];
-    ps1[3 * e + 0] = run; ps1[3 * e + 1] = (int32_t)nk; ps1[3 * e + 2] = (int32_t)kk;
-    ps2[3 * e + 0] = run; ps2[3 * e + 1] = (int32_t)kk; ps2[3 * e + 2] = (int32_t)nk;
+  if (tid < E) {
+    const int32_t base = tot[tid] - run;  // exclusive prefix
+    offsets[tid] = base;
+    if (tid == E - 1) offsets[E] = tot[tid];
+    ps1[3 * tid + 0] = run; ps1[3 * tid + 1] = (int32_t)nk; ps1[3 * tid + 2] = (int32_t)kk;
+    ps2[3 * tid + 0] = run; ps2[3 * tid + 1] = (int32_t)kk; ps2[3 * tid + 2] = (int32_t)nk;
   }
   __shared__ int32_t base_of[kScanThreads];
-  if (e < E) base_of[e] = tot[e] - run;
+  if (tid < E) base_of[tid] = tot[tid] - run;
   __syncthreads();
   // pass 2: shift every chunk base by its expert's offset (coalesced)
-  for (int64_t i = threadIdx.x; i < nchunks * E; i += kScanThreads) counts[i] += base_of[i % E];
+  if (one_slab) {
+    for (int64_t i = tid; i < nchunks * E; i += kScanThreads) counts[i] = slab[i] + base_of[i % E];
+  } else {
+    for (int64_t i = tid; i < nchunks * E; i += kScanThreads) counts[i] += base_of[i % E];
+  }
 }
 
 __global__ __launch_bounds__(kChunk) void moe_scatter(const int32_t* __restrict__ ids, int64_t n,

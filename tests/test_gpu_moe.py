@@ -28,7 +28,9 @@ def gpu_routing(ids_dev, E, n, k):
 
 
 @pytest.mark.parametrize("T,E,topk,seed", [(4096, 64, 8, 0), (1, 4, 1, 1), (7, 5, 3, 2),
-                                           (1000, 256, 8, 3), (3, 1024, 2, 4)])
+                                           (1000, 256, 8, 3), (3, 1024, 2, 4),
+                                           # chunk counts over several LDS slabs of the scan
+                                           (16384, 256, 8, 6), (20000, 1024, 8, 7), (5000, 3, 2, 8)])
 def test_routing_bit_exact(T, E, topk, seed):
     ids = synth.zipf_topk_ids(T, E, topk, seed=seed)
     got = [t.cpu().numpy() for t in gpu_routing(ids.to(DEV), E, 2048, 7168)]
