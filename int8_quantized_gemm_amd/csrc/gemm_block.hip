@@ -95,23 +95,6 @@ __device__ __forceinline__ f32x4 mfma_fp8_k128(const i32x8& a, const i32x8& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
 }
 
-// One 32-wide K block of a 16x16x128 MFMA on its own. The MX-scaled form
-// takes one E8M0 scale byte per lane and operand, lane r + 16 kb supplying
-// block kb's scale of row r, in the instruction's K order (lane group g
-// holds K [16g, 16g+16) in its first four registers and [64+16g, 64+16g+16)
-// in its last four; block kb is K [32kb, 32kb+32)). With byte 127 (2^0) in
-// lane group s and byte 0 (2^-127) elsewhere, on both operands, block s is
-// multiplied by exactly 1 and every other block by 2^-254, which puts each of
-// their products (at most 448^2 * 32 < 2^23 per block) below half the
-// smallest float32 subnormal: they contribute exactly zero, and the result
-// is block s's partial product with no VALU masking of the operands.
-__device__ __forceinline__ int block_selector(int g, int s) { return g == s ? 127 : 0; }
-
-__device__ __forceinline__ f32x4 mfma_block(const i32x8& w, const i32x8& a, int sel) {
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, a, z, 0, 0, 0, sel, 0, sel);
-}
-
 __device__ __forceinline__ f32x4 mfma_fp8_k32(long a, long b) {
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, z, 0, 0, 0);
@@ -747,6 +730,30 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile(TileParams p) {
 // ------------------------------------------------------------------------------
 // Skinny (decode) kernel
 // ------------------------------------------------------------------------------
+// A 16x16x128 fragment (lane group g: chunk bytes [16g, 16g+16) in dwords
+// 0..3, [64+16g, 64+16g+16) in dwords 4..7) regrouped into four 16x16x32
+// operands, one per 32-wide K block: v_permlane32_swap exchanges the upper
+// 32 lanes of its first operand with the lower 32 lanes of its second, so
+// swapping dwords 0, 1, 4, 5 with dwords 2, 3, 6, 7 that way leaves in dwords
+// 2s and 2s + 1 of lane group g the chunk bytes [32s + 16 (g & 1) +
+// 8 (g >> 1), +8): each block's 32 bytes spread over the four lane groups.
+// The other operand must hold the same bytes per lane group.
+__device__ __forceinline__ void regroup_blocks(i32x8& f) {
+  constexpr int lo[4] = {0, 1, 4, 5};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int d = lo[i];
+    const auto r = __builtin_amdgcn_permlane32_swap(f[d], f[d + 2], false, false);
+    f[d] = (int)r[0];
+    f[d + 2] = (int)r[1];
+  }
+}
+
+// 16x16x32 operand of block s from a regrouped fragment
+__device__ __forceinline__ long dword_pair(const i32x8& f, int s) {
+  return (long)(uint32_t)f[2 * s] | ((long)(uint32_t)f[2 * s + 1] << 32);
+}
+
 template <int KS>
 struct Frag;
 template <>
@@ -1105,7 +1112,9 @@ __device__ __forceinline__ void stage_rows(const TileParams& p, uint32_t a_pitch
 // LDS: activation rows at a pitch of K + 16 bytes (sixteen lanes reading one
 // K offset of sixteen rows hit sixteen bank groups), then the scale rows,
 // then the waves' partials.
-template <int KS, int NW, int R>
+// DA: weight chunks a wave issues before its first MFMA; each later chunk is
+// issued while the one DA before it is computed (DA = R: all up front).
+template <int KS, int NW, int R, int DA>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, NW / 4)))
 void gemm_stream_sa(TileParams p) {
   constexpr int KSUB = 128 / KS;
@@ -1135,38 +1144,54 @@ void gemm_stream_sa(TileParams p) {
   asm volatile("" ::: "memory");
   const int64_t nrow = n0 + r16 < N ? n0 + r16 : N - 1;
   const uint8_t* wp = p.W + nrow * K + 16 * g;
+  static_assert(DA >= 1 && DA <= R, "chunks issued ahead");
   i32x8 wf[R];
-#pragma unroll
-  for (int u = 0; u < R; ++u) {
-    // unconditional (clamped) loads: exactly 2R of them follow the copies
+  auto issue_w = [&](int u) {
+    // unconditional (clamped) loads: exactly 2 DA of them follow the copies
     const int c = c_b + u < NC - 1 ? c_b + u : NC - 1;
     wf[u] = gload_halves(wp + (int64_t)c * 128);
-  }
-  // the copies were issued before the 2R weight loads, and loads complete in
-  // order: at most 2R outstanding means this wave's copies have landed. The
-  // bare barrier (no fence) keeps the weight loads in flight across it.
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * R) : "memory");
+  };
+#pragma unroll
+  for (int u = 0; u < DA; ++u) issue_w(u);
+  // the copies were issued before the 2 DA weight loads, and loads complete
+  // in order: at most 2 DA outstanding means this wave's copies have landed.
+  // The bare barrier (no fence) keeps the weight loads in flight across it.
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DA) : "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   const int arow = r16 < M ? r16 : (int)M - 1;  // rows past M repeat the last (never stored)
-  const uint8_t* al = sA + arow * a_pitch + 16 * g;
+  // 32-wide blocks: the regrouped weight fragment's bytes of every block,
+  // 8 at 32s + 16 (g & 1) + 8 (g >> 1) per lane group
+  const uint8_t* al = sA + arow * a_pitch + (KS == 32 ? 16 * (g & 1) + 8 * (g >> 1) : 16 * g);
   const float* sl = reinterpret_cast<const float*>(sS) + arow * KB;
 #pragma unroll
   for (int u = 0; u < R; ++u) {
     const int c = c_b + u;
     if (c >= c_e) break;
-    const i32x4 lo = *reinterpret_cast<const i32x4*>(al + c * 128);
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(al + c * 128 + 64);
-    const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    if (u + DA < R) issue_w(u + DA);
+    i32x8 af;
+    if constexpr (KS == 32) {
+      regroup_blocks(wf[u]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int2 v = *reinterpret_cast<const int2*>(al + c * 128 + 32 * q);
+        af[2 * q] = v.x;
+        af[2 * q + 1] = v.y;
+      }
+    } else {
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(al + c * 128);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(al + c * 128 + 64);
+      af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
     f32x4 sa;
     if constexpr (KSUB == 4) sa = *reinterpret_cast<const f32x4*>(sl + c * 4);
     else sa[0] = sl[c];
 #pragma unroll
     for (int s = 0; s < KSUB; ++s) {
       const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsl), u * KSUB + s));
-      const f32x4 pr = KS == 128 ? mfma_fp8_k128(wf[u], af) : mfma_block(wf[u], af, block_selector(g, s));
+      const f32x4 pr = KS == 128 ? mfma_fp8_k128(wf[u], af) : mfma_fp8_k32(dword_pair(wf[u], s), dword_pair(af, s));
       acc = fma4s(pr, sa[s] * ws, acc);
     }
   }
@@ -1199,14 +1224,16 @@ void gemm_stream_sa(TileParams p) {
 // workgroup owns 64 weight rows (four 16-row blocks) and one of S K ranges of
 // Kc = K/S bytes: it copies the activation slice [M, Kc] and its scales into
 // LDS once (buffer->LDS, so the copies are in flight with the weight loads),
-// streams its 64 x Kc weight bytes (each wave issues all of its loads up
-// front), and writes its float32 partial [M, 64] for that K range;
+// streams its 64 x Kc weight bytes (each wave keeps one 128-byte chunk, two
+// above 32 rows, in flight ahead of its MFMAs; 128-wide blocks up to 32 rows
+// issue all of them up front), and writes its float32 partial [M, 64] for
+// that K range;
 // gemm_split_reduce then sums the S partials of every output in a fixed
 // order (deterministic), adds the bias and rounds.
-// MFMA columns: sixteen activation rows per MFMA (one per chunk and 16-row
-// block for 128-wide K blocks; for 32-wide blocks one per chunk, block and
-// 16-row block, each taking a single block through the scale selector of
-// mfma_block), so a lane's four outputs share one scale product.
+// MFMA columns: sixteen activation rows per MFMA (one 16x16x128 MFMA per
+// chunk and 16-row block for 128-wide K blocks; for 32-wide blocks four
+// 16x16x32 MFMAs, one per block, on the regrouped weight fragment), so a
+// lane's four outputs share one scale product.
 // LDS activation slice: dense [M, Kc], 16-byte piece j of row m stored at
 // piece position j ^ (m & 15) (Kc a multiple of 256 bytes keeps every row's
 // pieces inside the row); sixteen lanes reading one piece of sixteen rows
@@ -1300,33 +1327,51 @@ void gemm_split_mid(TileParams p, float* __restrict__ part, int Kc) {
   const int lc = h + (li / KSUB) * NP;
   const float wsl = p.Ws[nb * KB + kb0 + (lc < ncc ? lc : ncc - 1) * KSUB + li % KSUB];
   asm volatile("" ::: "memory");
+  // The first DA chunks are issued here, each later one while the chunk DA
+  // before it is computed: issued all up front, the loads stalled the wave at
+  // issue until most of their bytes had arrived, so the MFMA work only began
+  // after the weight stream (N = 4096, K = 7168, 32-wide blocks, M = 17 / 24
+  // / 48 / 64: 12.85 / 13.02 / 14.55 / 16.11 us all up front, 11.75 / 12.06 /
+  // 13.61 / 14.68 us one ahead, 11.90 / 12.28 / 13.03 / 14.20 us two ahead).
+  // 128-wide blocks have a quarter of the MFMA work: up to 32 rows all up
+  // front is faster there (M = 32: 12.00 against 12.20 us one ahead), at 64
+  // rows two ahead (13.83 -> 13.35 us).
+  constexpr int DA0 = MT > 2 ? 2 : (KS == 32 ? 1 : R);
+  constexpr int DA = DA0 < R ? DA0 : R;
   i32x8 wf[R];
-#pragma unroll
-  for (int u = 0; u < R; ++u) {
+  auto issue_w = [&](int u) {
     const int cc0 = h + u * NP;
     const int cc = cc0 < ncc ? cc0 : ncc - 1;
     wf[u] = gload_halves(wp + (int64_t)cc * 128);
-  }
+  };
+#pragma unroll
+  for (int u = 0; u < DA; ++u) issue_w(u);
   // the copies were issued first and loads complete in order: once at most
-  // 2R (weight halves) + 1 (scales) remain, this wave's copies have landed;
+  // 2 DA (weight halves) + 1 (scales) remain, this wave's copies have landed;
   // the barrier without a fence keeps the weight loads in flight across it
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * R + 1) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DA + 1) : "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
   // LDS byte offsets of this lane's fragment pieces and scales for its
-  // first chunk (h), per 16-row block t. Chunk h + NP u (NP = 2) adds 256 u
-  // bytes to every piece offset: piece (8 cc + x) ^ key with x = 8h + 4f + g
-  // < 16 and key < 16 is 16 u + (x ^ key). Rows past M repeat the last row
-  // (never stored).
+  // first chunk (h), per 16-row block t. 128-wide blocks: the two 16-byte
+  // pieces x = 8h + 4f + g of the 16x16x128 fragment. 32-wide blocks: the
+  // four 8-byte halves (g >> 1) of pieces x = 8h + 2s + (g & 1), block s's
+  // bytes of lane group g in the regrouped weight fragment. Chunk h + NP u
+  // (NP = 2) adds 256 u bytes to every offset: piece (8 cc + x) ^ key with
+  // x < 16 and key < 16 is 16 u + (x ^ key). Rows past M repeat the last
+  // row (never stored).
   static_assert(NP == 2, "piece offsets assume two chunk parities");
-  uint32_t aoff[MT][2], soff[MT];
+  constexpr int NA = KS == 32 ? 4 : 2;
+  uint32_t aoff[MT][NA], soff[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int m = 16 * t + r16 < M ? 16 * t + r16 : (int)M - 1;
     const int key = m & 15;
 #pragma unroll
-    for (int f = 0; f < 2; ++f) aoff[t][f] = (uint32_t)(m * Kc + 16 * ((8 * h + 4 * f + g) ^ key));
+    for (int f = 0; f < NA; ++f)
+      aoff[t][f] = KS == 32 ? (uint32_t)(m * Kc + 16 * ((8 * h + 2 * f + (g & 1)) ^ key) + 8 * (g >> 1))
+                            : (uint32_t)(m * Kc + 16 * ((8 * h + 4 * f + g) ^ key));
     soff[t] = (uint32_t)((m * kbc + h * KSUB) * 4);
   }
   const uint8_t* sSb = reinterpret_cast<const uint8_t*>(sS);
@@ -1334,9 +1379,18 @@ void gemm_split_mid(TileParams p, float* __restrict__ part, int Kc) {
   i32x8 afb[2];
   f32x4 sab[2];
   auto load = [&](int u, int t, int b) {
-    const i32x4 lo = *reinterpret_cast<const i32x4*>(sA + aoff[t][0] + 256 * u);
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(sA + aoff[t][1] + 256 * u);
-    afb[b] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    if constexpr (KS == 32) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int2 v = *reinterpret_cast<const int2*>(sA + aoff[t][q] + 256 * u);
+        afb[b][2 * q] = v.x;
+        afb[b][2 * q + 1] = v.y;
+      }
+    } else {
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(sA + aoff[t][0] + 256 * u);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(sA + aoff[t][1] + 256 * u);
+      afb[b] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
     if constexpr (KSUB == 4) sab[b] = *reinterpret_cast<const f32x4*>(sSb + soff[t] + 32 * u);
     else sab[b][0] = *reinterpret_cast<const float*>(sSb + soff[t] + 8 * u);
   };
@@ -1348,6 +1402,8 @@ void gemm_split_mid(TileParams p, float* __restrict__ part, int Kc) {
   for (int u = 0; u < R; ++u) {
     const int cc = h + u * NP;
     if (cc >= ncc) break;
+    if (u + DA < R) issue_w(u + DA);
+    if constexpr (KS == 32) regroup_blocks(wf[u]);
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const int b = (u * MT + t) & 1;
@@ -1356,7 +1412,8 @@ void gemm_split_mid(TileParams p, float* __restrict__ part, int Kc) {
 #pragma unroll
       for (int s = 0; s < KSUB; ++s) {
         const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsl), u * KSUB + s));
-        const f32x4 pr = KS == 32 ? mfma_block(wf[u], afb[b], block_selector(g, s)) : mfma_fp8_k128(wf[u], afb[b]);
+        const f32x4 pr = KS == 32 ? mfma_fp8_k32(dword_pair(wf[u], s), dword_pair(afb[b], s))
+                                  : mfma_fp8_k128(wf[u], afb[b]);
         acc[t] = fma4s(pr, sab[b][s] * ws, acc[t]);
       }
     }
@@ -1470,9 +1527,16 @@ hipError_t raise_lds_limit(const void* kern, std::atomic<uint64_t>& done) {
 
 template <int KS, int R>
 hipError_t launch_stream_sa_r(const TileParams& tp, hipStream_t st) {
-  const auto kern = gemm_stream_sa<KS, kStreamSaNW, R>;
-  static std::atomic<uint64_t> lds_raised{0};
-  const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kern), lds_raised);
+  // from 8 rows on (16 with 128-wide blocks, a quarter of the MFMA work),
+  // one chunk issued ahead of the MFMAs instead of all up front (N = 4096,
+  // K = 7168, 32-wide blocks: M = 8 / 16 8.28 / 9.25 -> 8.02 / 8.68 us;
+  // 128-wide blocks M = 16 8.67 -> 8.48 us); with fewer rows the MFMA work is
+  // too short to hide and all up front is faster (128-wide M = 1 / 4 / 8:
+  // 7.33 / 7.47 / 7.77 us against 7.75 / 7.82 / 7.92 us)
+  const bool ahead = tp.M >= (KS == 32 ? 8 : 16);
+  const auto kern = ahead ? gemm_stream_sa<KS, kStreamSaNW, R, 1> : gemm_stream_sa<KS, kStreamSaNW, R, R>;
+  static std::atomic<uint64_t> lds_raised[2]{};
+  const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kern), lds_raised[ahead]);
   if (e != hipSuccess) return e;
   if ((tp.N + 15) / 16 > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   const unsigned lds = (unsigned)stream_sa_lds(tp.M, tp.K, tp.KB);
