@@ -1313,10 +1313,10 @@ void gemm_split_mid(TileParams p, float* __restrict__ part, int Kc) {
       }
     }
   }
-  // ---- this wave's weight chunks (row block rb, chunks h, h + NP, ...), all
-  // issued before any wait; lane group g holds bytes [16g, 16g+16) and
-  // [64+16g, 64+16g+16) of each chunk (the MX-scaled MFMA's K order, in which
-  // 32-wide block s of the chunk is the instruction's block s)
+  // ---- this wave's weight chunks (row block rb, chunks h, h + NP, ...); lane
+  // group g holds bytes [16g, 16g+16) and [64+16g, 64+16g+16) of each chunk
+  // (the 16x16x128 MFMA's K order; regrouped per 32-wide block for the
+  // 16x16x32 MFMAs)
   const int64_t nrow = n0 + 16 * rb + r16 < N ? n0 + 16 * rb + r16 : N - 1;
   const uint8_t* wp = p.W + nrow * K + k0 + 16 * g;
   int64_t nb = (n0 + 16 * rb) / p.bn;
