@@ -202,14 +202,20 @@ def bench_prefill_variants(torch, q8, synth, pre, reps):
     return out
 
 
-def batched_us(torch, launch, copies, reps, warmup=3):
+def batched_us(torch, launch, copies, reps, warmup=3, warmup_s=0.05):
     """Per-launch time of ``copies`` back-to-back launches (each on its own
     buffers) between one pair of HIP events on the launch stream, median over
     ``reps`` batches. Batching amortises the event overhead that would
-    otherwise dominate kernels of a few microseconds."""
-    for i in range(warmup):
+    otherwise dominate kernels of a few microseconds. Untimed warm-up: at
+    least ``warmup`` batches and ``warmup_s`` seconds of them, so that the
+    clock has ramped up after the host-side set-up between measurements."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t0 < warmup_s:
         for c in range(copies):
             launch(c)
+        i += 1
+    torch.cuda.synchronize()
     vals = []
     for _ in range(reps):
         s = torch.cuda.Event(enable_timing=True)
@@ -271,12 +277,16 @@ def bench_decode(torch, q8, synth, reps):
         def quant(c):
             q8.quant_8bit(x, aq[c], As[c], blk, EPS, -448.0, 448.0, True)
 
-        def gemm(c):
-            q8.blockwise_scaled_mm(aq[c], W_list[c], As[c], Ws_list[c], torch.bfloat16,
-                                   block=(blk, blk), out=D)
-
         for c in range(copies):
             quant(c)
+        # the launches are bound once (checked and marshalled up front): a
+        # decode GEMM takes about as long as one checked Python call
+        calls = [q8.bind_blockwise_scaled_mm(aq[c], W_list[c], As[c], Ws_list[c], D, block=(blk, blk))
+                 for c in range(copies)]
+
+        def gemm(c):
+            calls[c]()
+
         g = batched_us(torch, gemm, copies, reps)
         qv = graph_us(torch, quant, copies, reps)
         nbytes = wbytes + Ws.numel() * 4 + M * K + M * (K // blk) * 4 + M * N * 2
@@ -287,8 +297,9 @@ def bench_decode(torch, q8, synth, reps):
                         "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
                         "tflops": round(2.0 * M * N * K / (g["median"] * 1e-6) / 1e12, 2)}
     out["weight_copies_rotated"] = copies
-    out["timing"] = ("GEMM: HIP events around batches of back-to-back launches, one weight copy each; "
-                     "quant (a few-microsecond kernel): the same launches replayed from a HIP graph")
+    out["timing"] = ("GEMM: HIP events around batches of back-to-back launches, one weight copy each, "
+                     "each launch a pre-marshalled C-ABI call; quant (a few-microsecond kernel): the "
+                     "same launches replayed from a HIP graph")
     return out
 
 
@@ -403,8 +414,9 @@ def bench_e8m0(torch, q8, synth, reps):
         asd = torch.empty((Md, K // 32), dtype=torch.uint8, device=dev)
         q8.quant_8bit(xd, aqd, asd, 32, EPS, -448.0, 448.0, 2)
         Dd = torch.empty((Md, N), dtype=torch.bfloat16, device=dev)
-        g = batched_us(torch, lambda c: q8.blockwise_scaled_mm_e8m0(aqd, Wl[c], asd, Wsl[c], block_n=32,
-                                                                      out=Dd), copies, 30)
+        calls = [q8.bind_blockwise_scaled_mm_e8m0(aqd, Wl[c], asd, Wsl[c], Dd, block_n=32)
+                 for c in range(copies)]
+        g = batched_us(torch, lambda c: calls[c](), copies, 30)
         nbytes = N * K + Ws0.numel() + Md * K + Md * (K // 32) + Md * N * 2
         gbs = nbytes / (g["median"] * 1e-6) / 1e9
         dec[f"M{Md}"] = {"gemm_us": round(g["median"], 3), "algorithmic_bytes": nbytes,

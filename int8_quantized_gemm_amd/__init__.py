@@ -203,6 +203,24 @@ def _workspace(dev, nbytes: int):
     return buf.data_ptr(), buf.numel()
 
 
+def _workspace_for(dev, nbytes: int, own: bool):
+    """(pointer, size, owner): the shared cached workspace, or with ``own`` a
+    buffer of its own (the cache may be reallocated by a later, larger call)."""
+    if not own:
+        return (*_workspace(dev, nbytes), None)
+    if nbytes == 0:
+        return None, 0, None
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    return buf.data_ptr(), nbytes, buf
+
+
+def _bound(fn, args, keep):
+    def call():
+        _check(fn(*args))
+    call.keep = keep
+    return call
+
+
 # ---------------------------------------------------------------------------
 def quant_8bit(input: torch.Tensor, output_q: torch.Tensor, output_s: torch.Tensor,
                group_size: int, eps: float = 1e-10, fp8_min: float = -448.0,
@@ -267,7 +285,7 @@ def quant_8bit(input: torch.Tensor, output_q: torch.Tensor, output_s: torch.Tens
 def blockwise_scaled_mm(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torch.Tensor,
                         scales_b: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
                         bias: torch.Tensor | None = None, block=(128, 128),
-                        out: torch.Tensor | None = None) -> torch.Tensor:
+                        out: torch.Tensor | None = None, *, _own_workspace: bool = False) -> torch.Tensor:
     """Block-scaled FP8 GEMM ``D = A @ W.T`` with per-(row, K block) ``scales_a``
     [M, K/bk] and per-(bn x bk tile) ``scales_b`` [ceil(N/bn), K/bk]."""
     _contig(mat_a, mat_b, scales_a, scales_b, bias)
@@ -289,16 +307,19 @@ def blockwise_scaled_mm(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torc
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=dev)
     _contig(out)
-    ws, wsb = _workspace(dev, _ws_size(_bmm_ws, M, N, K, bn, bk))
-    _check(_bmm(_ptr(mat_a), _ptr(scales_a), _ptr(mat_b), _ptr(scales_b), _ptr(bias), _ptr(out),
-                _dt(out.dtype), M, N, K, bn, bk, ws, wsb, _stream(dev)))
+    ws, wsb, keep = _workspace_for(dev, _ws_size(_bmm_ws, M, N, K, bn, bk), _own_workspace)
+    args = (_ptr(mat_a), _ptr(scales_a), _ptr(mat_b), _ptr(scales_b), _ptr(bias), _ptr(out),
+            _dt(out.dtype), M, N, K, bn, bk, ws, wsb, _stream(dev))
+    if _own_workspace:
+        return _bound(_bmm, args, (keep, mat_a, mat_b, scales_a, scales_b, bias, out))
+    _check(_bmm(*args))
     return out
 
 
 def blockwise_scaled_mm_e8m0(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torch.Tensor,
                              scales_b: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
                              bias: torch.Tensor | None = None, block_n: int = 32,
-                             out: torch.Tensor | None = None) -> torch.Tensor:
+                             out: torch.Tensor | None = None, *, _own_workspace: bool = False) -> torch.Tensor:
     """Block-scaled FP8 GEMM with E8M0 (power-of-two) scales on both operands:
     ``scales_a`` [M, K/32] and ``scales_b`` [ceil(N/block_n), K/32] as uint8
     (or torch.float8_e8m0fnu) bytes, 32-wide K blocks."""
@@ -322,10 +343,30 @@ def blockwise_scaled_mm_e8m0(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a:
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=dev)
     _contig(out)
-    ws, wsb = _workspace(dev, _ws_size(_bmm8_ws, M, N, K, block_n))
-    _check(_bmm8(_ptr(mat_a), _ptr(scales_a), _ptr(mat_b), _ptr(scales_b), _ptr(bias), _ptr(out),
-                 _dt(out.dtype), M, N, K, block_n, ws, wsb, _stream(dev)))
+    ws, wsb, keep = _workspace_for(dev, _ws_size(_bmm8_ws, M, N, K, block_n), _own_workspace)
+    args = (_ptr(mat_a), _ptr(scales_a), _ptr(mat_b), _ptr(scales_b), _ptr(bias), _ptr(out),
+            _dt(out.dtype), M, N, K, block_n, ws, wsb, _stream(dev))
+    if _own_workspace:
+        return _bound(_bmm8, args, (keep, mat_a, mat_b, scales_a, scales_b, bias, out))
+    _check(_bmm8(*args))
     return out
+
+
+def bind_blockwise_scaled_mm(mat_a, mat_b, scales_a, scales_b, out, bias=None, block=(128, 128)):
+    """Checks and marshals one ``blockwise_scaled_mm`` call once and returns a
+    function of no arguments that repeats exactly that C call (same buffers,
+    the stream current at bind time, a workspace of its own): for timing
+    loops, where the per-call host-side checks would otherwise be timed with
+    kernels of a few microseconds. The returned function keeps the tensors
+    alive; their contents may change between calls."""
+    return blockwise_scaled_mm(mat_a, mat_b, scales_a, scales_b, out.dtype, bias, block, out,
+                               _own_workspace=True)
+
+
+def bind_blockwise_scaled_mm_e8m0(mat_a, mat_b, scales_a, scales_b, out, bias=None, block_n=32):
+    """``bind_blockwise_scaled_mm`` for ``blockwise_scaled_mm_e8m0``."""
+    return blockwise_scaled_mm_e8m0(mat_a, mat_b, scales_a, scales_b, out.dtype, bias, block_n, out,
+                                    _own_workspace=True)
 
 
 def scaled_mm_int8(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torch.Tensor | None,

@@ -1825,15 +1825,13 @@ hipError_t launch_blockwise(const BlockGemmArgs& a, hipStream_t st) {
     // staging the activation rows once per workgroup beats every wave reading
     // them from L2 at any row count with 128-wide blocks (N = 4096, K = 7168,
     // M = 1 / 2 / 4 / 7: 8.03 / 8.69 / 8.99 / 9.74 us unstaged, 7.28 / 7.35 /
-    // 7.55 / 7.76 us staged), and with 32-wide blocks beats the packed kernel
-    // below from 3 rows on (M = 1 / 2 / 3 / 4: 7.92 / 7.97 / 8.15 / 8.21 us
-    // packed, 8.01 / 7.95 / 7.90 / 8.01 us staged)
-    const int64_t sa_min = a.bk == 32 ? 3 : 1;
-    if (a.M >= sa_min && stream_sa_fits(a.M, a.K, tp.KB) && (uintptr_t)a.A % 16 == 0 &&
-        (uintptr_t)a.As % 16 == 0)
+    // 7.55 / 7.76 us staged), and with 32-wide blocks (16x16x32 MFMAs) beats
+    // the packed kernel below at any row count too (M = 1 / 2: 7.87 / 7.97 us
+    // packed, 7.67 / 7.70 us staged)
+    if (stream_sa_fits(a.M, a.K, tp.KB) && (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.As % 16 == 0)
       return a.bk == 128 ? launch_stream_sa<128>(tp, st) : launch_stream_sa<32>(tp, st);
-    // 32-wide blocks, up to 8 rows (2 when the staged kernel fits): four rows'
-    // block partials per MFMA
+    // 32-wide blocks, up to 8 rows, where the staged kernel does not apply
+    // (K not a multiple of 1024): four rows' block partials per MFMA
     if (a.bk == 32 && a.M <= 8) return launch_stream_pk(tp, st);
     return a.bk == 128 ? launch_stream<128>(tp, st) : launch_stream<32>(tp, st);
   }

@@ -72,7 +72,7 @@ def test_decode_block32_ue8m0(M):
                                    (7, 4096, 7168), (1, 4096, 7168), (3, 520, 3072)])
 @pytest.mark.parametrize("bk", [128, 32])
 def test_decode_shared_activation_shapes(M, N, K, bk):
-    """Up to 16 activation rows with 128-wide blocks (3..16 with 32-wide) and
+    """Up to 16 activation rows (either block width) and
     K a multiple of 1024 take the kernel that stages the activations once per
     workgroup: waves without K chunks (K = 1024), one, two, four, seven or
     eight chunks per wave, ragged N, the largest K it accepts (8192)."""
@@ -91,6 +91,13 @@ def test_decode_packed_two_row_groups(M):
     """5..8 rows, 32-wide blocks, K not a multiple of 1024: the packed kernel
     with two four-row MFMA groups (the staged kernel does not apply)."""
     run_case(M, 520, 1536, 32, 32, ue=True, bias=True, seed=M)
+
+
+@pytest.mark.parametrize("M,K", [(1, 1536), (2, 2560), (4, 7296)])
+def test_decode_packed_one_row_group(M, K):
+    """1..4 rows, 32-wide blocks, K not a multiple of 1024: the packed kernel
+    with one four-row MFMA group (rows past M padded)."""
+    run_case(M, 520, K, 32, 32, ue=True, bias=True, seed=M + K)
 
 
 @pytest.mark.parametrize("M,N,K,bn,bk", [(17, 1000, 1024, 128, 128), (33, 4096, 7168, 32, 32),
@@ -318,3 +325,47 @@ def test_split_only_half_empty_last_rounds():
         assert (ws > 0) == want, (M, N, cus, ws)
         if want:
             assert ws >= R * 256 * 256 * 4 + R * 4
+
+
+@pytest.mark.parametrize("M", [1, 64, 768])
+def test_bound_calls_repeat_the_checked_call(M):
+    """bind_blockwise_scaled_mm and bind_blockwise_scaled_mm_e8m0 return a
+    call that repeats the checked one on the same buffers with a workspace of
+    its own: one row (staged kernel), 64 rows (split K, partials in the
+    workspace) and 768 rows (33 tiles split in K, flags in the workspace).
+    Outputs equal the checked call's bit for bit, on each of two repeats, and
+    follow new operand contents written into the same buffers."""
+    m = q8()
+    N, K = 2816, 2048
+    Wq, Ws = synth.fp8_block_weights(N, K, 32, 32, seed=M)
+    Wd, Wsd = Wq.to(DEV).view(torch.float8_e4m3fn), Ws.to(DEV)
+    _, aq, As = _quantized(M, K, 32, seed=M)
+    ref = m.blockwise_scaled_mm(aq, Wd, As, Wsd, torch.bfloat16, block=(32, 32))
+    d = torch.empty_like(ref)
+    call = m.bind_blockwise_scaled_mm(aq, Wd, As, Wsd, d, block=(32, 32))
+    for _ in range(2):
+        d.zero_()
+        call()
+        sync()
+        assert torch.equal(d, ref)
+    _, aq2, As2 = _quantized(M, K, 32, seed=M + 1)
+    aq.copy_(aq2)
+    As.copy_(As2)
+    call()
+    sync()
+    assert torch.equal(d, m.blockwise_scaled_mm(aq2, Wd, As2, Wsd, torch.bfloat16, block=(32, 32)))
+
+    W8, Ws8 = synth.fp8_block_weights_e8m0(N, K, 32, 32, seed=M)
+    W8d, Ws8d = W8.to(DEV).view(torch.float8_e4m3fn), Ws8.to(DEV)
+    x = synth.activations(M, K, "bf16", seed=M).to(DEV)
+    aq8 = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=DEV)
+    as8 = torch.empty((M, K // 32), dtype=torch.uint8, device=DEV)
+    m.quant_8bit(x, aq8, as8, 32, EPS, -448.0, 448.0, 2)
+    ref8 = m.blockwise_scaled_mm_e8m0(aq8, W8d, as8, Ws8d, torch.bfloat16, block_n=32)
+    d8 = torch.empty_like(ref8)
+    call8 = m.bind_blockwise_scaled_mm_e8m0(aq8, W8d, as8, Ws8d, d8, block_n=32)
+    for _ in range(2):
+        d8.zero_()
+        call8()
+        sync()
+        assert torch.equal(d8, ref8)
