@@ -281,8 +281,10 @@ def bench_decode(torch, q8, synth, reps):
             quant(c)
         # the launches are bound once (checked and marshalled up front): a
         # decode GEMM takes about as long as one checked Python call
-        calls = [q8.bind_blockwise_scaled_mm(aq[c], W_list[c], As[c], Ws_list[c], D, block=(blk, blk))
-                 for c in range(copies)]
+        ws = torch.empty(max(1, q8.blockwise_scaled_mm_workspace_size(M, N, K, blk, blk)),
+                         dtype=torch.uint8, device=dev)
+        calls = [q8.bind_blockwise_scaled_mm(aq[c], W_list[c], As[c], Ws_list[c], D, block=(blk, blk),
+                                             workspace=ws) for c in range(copies)]
 
         def gemm(c):
             calls[c]()
@@ -414,7 +416,9 @@ def bench_e8m0(torch, q8, synth, reps):
         asd = torch.empty((Md, K // 32), dtype=torch.uint8, device=dev)
         q8.quant_8bit(xd, aqd, asd, 32, EPS, -448.0, 448.0, 2)
         Dd = torch.empty((Md, N), dtype=torch.bfloat16, device=dev)
-        calls = [q8.bind_blockwise_scaled_mm_e8m0(aqd, Wl[c], asd, Wsl[c], Dd, block_n=32)
+        wsd = torch.empty(max(1, q8.blockwise_scaled_mm_e8m0_workspace_size(Md, N, K, 32)),
+                          dtype=torch.uint8, device=dev)
+        calls = [q8.bind_blockwise_scaled_mm_e8m0(aqd, Wl[c], asd, Wsl[c], Dd, block_n=32, workspace=wsd)
                  for c in range(copies)]
         g = batched_us(torch, lambda c: calls[c](), copies, 30)
         nbytes = N * K + Ws0.numel() + Md * K + Md * (K // 32) + Md * N * 2

@@ -203,15 +203,20 @@ def _workspace(dev, nbytes: int):
     return buf.data_ptr(), buf.numel()
 
 
-def _workspace_for(dev, nbytes: int, own: bool):
-    """(pointer, size, owner): the shared cached workspace, or with ``own`` a
-    buffer of its own (the cache may be reallocated by a later, larger call)."""
-    if not own:
+def _workspace_for(dev, nbytes: int, own):
+    """(pointer, size, owner): the shared cached workspace; with ``own`` True a
+    buffer of its own (the cache may be reallocated by a later, larger call);
+    with ``own`` a uint8 device tensor, that tensor (at least ``nbytes``)."""
+    if own is False:
         return (*_workspace(dev, nbytes), None)
     if nbytes == 0:
         return None, 0, None
-    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    return buf.data_ptr(), nbytes, buf
+    if own is True:
+        own = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _need(own.dtype == torch.uint8 and own.is_contiguous() and own.numel() >= nbytes
+          and own.device == torch.device("cuda", dev),
+          f"workspace must be a contiguous uint8 tensor of at least {nbytes} bytes on the same device")
+    return own.data_ptr(), own.numel(), own
 
 
 def _bound(fn, args, keep):
@@ -285,7 +290,7 @@ def quant_8bit(input: torch.Tensor, output_q: torch.Tensor, output_s: torch.Tens
 def blockwise_scaled_mm(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torch.Tensor,
                         scales_b: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
                         bias: torch.Tensor | None = None, block=(128, 128),
-                        out: torch.Tensor | None = None, *, _own_workspace: bool = False) -> torch.Tensor:
+                        out: torch.Tensor | None = None, *, _own_workspace=False) -> torch.Tensor:
     """Block-scaled FP8 GEMM ``D = A @ W.T`` with per-(row, K block) ``scales_a``
     [M, K/bk] and per-(bn x bk tile) ``scales_b`` [ceil(N/bn), K/bk]."""
     _contig(mat_a, mat_b, scales_a, scales_b, bias)
@@ -310,7 +315,7 @@ def blockwise_scaled_mm(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torc
     ws, wsb, keep = _workspace_for(dev, _ws_size(_bmm_ws, M, N, K, bn, bk), _own_workspace)
     args = (_ptr(mat_a), _ptr(scales_a), _ptr(mat_b), _ptr(scales_b), _ptr(bias), _ptr(out),
             _dt(out.dtype), M, N, K, bn, bk, ws, wsb, _stream(dev))
-    if _own_workspace:
+    if _own_workspace is not False:
         return _bound(_bmm, args, (keep, mat_a, mat_b, scales_a, scales_b, bias, out))
     _check(_bmm(*args))
     return out
@@ -319,7 +324,7 @@ def blockwise_scaled_mm(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torc
 def blockwise_scaled_mm_e8m0(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torch.Tensor,
                              scales_b: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
                              bias: torch.Tensor | None = None, block_n: int = 32,
-                             out: torch.Tensor | None = None, *, _own_workspace: bool = False) -> torch.Tensor:
+                             out: torch.Tensor | None = None, *, _own_workspace=False) -> torch.Tensor:
     """Block-scaled FP8 GEMM with E8M0 (power-of-two) scales on both operands:
     ``scales_a`` [M, K/32] and ``scales_b`` [ceil(N/block_n), K/32] as uint8
     (or torch.float8_e8m0fnu) bytes, 32-wide K blocks."""
@@ -346,27 +351,44 @@ def blockwise_scaled_mm_e8m0(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a:
     ws, wsb, keep = _workspace_for(dev, _ws_size(_bmm8_ws, M, N, K, block_n), _own_workspace)
     args = (_ptr(mat_a), _ptr(scales_a), _ptr(mat_b), _ptr(scales_b), _ptr(bias), _ptr(out),
             _dt(out.dtype), M, N, K, block_n, ws, wsb, _stream(dev))
-    if _own_workspace:
+    if _own_workspace is not False:
         return _bound(_bmm8, args, (keep, mat_a, mat_b, scales_a, scales_b, bias, out))
     _check(_bmm8(*args))
     return out
 
 
-def bind_blockwise_scaled_mm(mat_a, mat_b, scales_a, scales_b, out, bias=None, block=(128, 128)):
+def blockwise_scaled_mm_workspace_size(M: int, N: int, K: int, bn: int, bk: int) -> int:
+    """Bytes of device workspace ``blockwise_scaled_mm`` takes for these sizes
+    on the current device (0: none)."""
+    return _ws_size(_bmm_ws, M, N, K, bn, bk)
+
+
+def blockwise_scaled_mm_e8m0_workspace_size(M: int, N: int, K: int, block_n: int = 32) -> int:
+    """Bytes of device workspace ``blockwise_scaled_mm_e8m0`` takes for these
+    sizes on the current device (0: none)."""
+    return _ws_size(_bmm8_ws, M, N, K, block_n)
+
+
+def bind_blockwise_scaled_mm(mat_a, mat_b, scales_a, scales_b, out, bias=None, block=(128, 128),
+                             workspace=None):
     """Checks and marshals one ``blockwise_scaled_mm`` call once and returns a
     function of no arguments that repeats exactly that C call (same buffers,
-    the stream current at bind time, a workspace of its own): for timing
-    loops, where the per-call host-side checks would otherwise be timed with
-    kernels of a few microseconds. The returned function keeps the tensors
-    alive; their contents may change between calls."""
+    the stream current at bind time): for timing loops, where the per-call
+    host-side checks would otherwise be timed with kernels of a few
+    microseconds. ``workspace``: a uint8 device tensor of at least
+    ``blockwise_scaled_mm_workspace_size`` bytes (calls bound to one tensor
+    share it and must run in one stream's order), or None for a buffer of
+    the call's own. The returned function keeps the tensors alive; their
+    contents may change between calls."""
     return blockwise_scaled_mm(mat_a, mat_b, scales_a, scales_b, out.dtype, bias, block, out,
-                               _own_workspace=True)
+                               _own_workspace=True if workspace is None else workspace)
 
 
-def bind_blockwise_scaled_mm_e8m0(mat_a, mat_b, scales_a, scales_b, out, bias=None, block_n=32):
+def bind_blockwise_scaled_mm_e8m0(mat_a, mat_b, scales_a, scales_b, out, bias=None, block_n=32,
+                                  workspace=None):
     """``bind_blockwise_scaled_mm`` for ``blockwise_scaled_mm_e8m0``."""
     return blockwise_scaled_mm_e8m0(mat_a, mat_b, scales_a, scales_b, out.dtype, bias, block_n, out,
-                                    _own_workspace=True)
+                                    _own_workspace=True if workspace is None else workspace)
 
 
 def scaled_mm_int8(mat_a: torch.Tensor, mat_b: torch.Tensor, scales_a: torch.Tensor | None,

@@ -333,8 +333,9 @@ def test_bound_calls_repeat_the_checked_call(M):
     call that repeats the checked one on the same buffers with a workspace of
     its own: one row (staged kernel), 64 rows (split K, partials in the
     workspace) and 768 rows (33 tiles split in K, flags in the workspace).
-    Outputs equal the checked call's bit for bit, on each of two repeats, and
-    follow new operand contents written into the same buffers."""
+    Outputs equal the checked call's bit for bit, on each of two repeats, with
+    a caller's workspace too (one short by a byte is refused), and follow new
+    operand contents written into the same buffers."""
     m = q8()
     N, K = 2816, 2048
     Wq, Ws = synth.fp8_block_weights(N, K, 32, 32, seed=M)
@@ -343,6 +344,17 @@ def test_bound_calls_repeat_the_checked_call(M):
     ref = m.blockwise_scaled_mm(aq, Wd, As, Wsd, torch.bfloat16, block=(32, 32))
     d = torch.empty_like(ref)
     call = m.bind_blockwise_scaled_mm(aq, Wd, As, Wsd, d, block=(32, 32))
+    need = m.blockwise_scaled_mm_workspace_size(M, N, K, 32, 32)
+    assert (need > 0) == (M > 16)
+    ws = torch.empty(max(1, need), dtype=torch.uint8, device=DEV)
+    d_ws = torch.empty_like(ref)
+    call_ws = m.bind_blockwise_scaled_mm(aq, Wd, As, Wsd, d_ws, block=(32, 32), workspace=ws)
+    call_ws()
+    sync()
+    assert torch.equal(d_ws, ref)
+    if need:
+        with pytest.raises(ValueError):
+            m.bind_blockwise_scaled_mm(aq, Wd, As, Wsd, d_ws, block=(32, 32), workspace=ws[:need - 1])
     for _ in range(2):
         d.zero_()
         call()
